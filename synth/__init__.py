@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for paged, variable-length attention.
+
+This module only *draws* inputs: per-sequence query and context lengths, a shuffled pool of
+physical blocks dealt into per-sequence block tables, and tensor values. It holds none of the
+attention arithmetic (no packing into offsets, no gather, no softmax, no task decomposition), so
+both the CPU oracle and the GPU path can consume what it returns without sharing any of the
+method's code.
+
+Workload shapes follow the pages' statement of the problem:
+  * paged KV pool of fixed-size blocks with an int32 block table, -1 for unused entries
+    (cann-recipes-infer Paged KV / Packed Sequence page, sections 2.2 and 3.1);
+  * one query token per sequence for decode (MindIE page, "Continuous Batching");
+  * 512-token prefill chunks over a cached prefix (MindIE page, "Prefill Chunking");
+  * packed variable-length prompts (cann-recipes-infer page, section 2.3).
+The pages' own datasets (ShareGPT-V3, an internal RAG trace) are not available; the length
+distributions below stand in for them.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "make_workload", "deal_block_table", "make_values",
+           "custom_workload"]
+
+
+@dataclass
+class Workload:
+    """Shapes and integer inputs of one synthetic batch (no tensor values)."""
+    name: str
+    seed: int
+    q_lens: np.ndarray          # int64 [N]  new query tokens per sequence
+    ctx_lens: np.ndarray        # int64 [N]  keys visible after this step's cache writes
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str                  # "bf16" or "fp32"
+    block_table: np.ndarray     # int32 [N, max_blocks_per_seq], -1 = unused entry
+    num_blocks: int             # physical blocks in the pool
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def deal_block_table(ctx_lens: np.ndarray, block_size: int, rng: np.random.Generator,
+                     pool_blocks: int | None = None, min_width: int = 1):
+    """Deal a seeded permutation of a block pool to each sequence's logical blocks, in order.
+
+    Sequence s needs ceil(ctx_s / block_size) blocks. The pool holds ``pool_blocks`` physical
+    blocks (default: exactly the total need). Entries past a sequence's need stay -1.
+    Returns (block_table int32 [N, width], pool size).
+    """
+    need = [(int(c) + block_size - 1) // block_size for c in ctx_lens]
+    total = int(sum(need))
+    nb = total if pool_blocks is None else int(pool_blocks)
+    if nb < total:
+        raise ValueError("pool smaller than the blocks the contexts need")
+    perm = rng.permutation(nb)
+    width = max(max(need) if need else 1, min_width)
+    table = np.full((len(need), width), -1, dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(need):
+        table[s, :n] = perm[pos:pos + n]
+        pos += n
+    return table, nb
+
+
+def _lengths(name: str, rng: np.random.Generator):
+    """Per-config length draws. Returns (q_lens, ctx_lens, Hq, Hkv, D, bs, dtype, pool)."""
+    if name == "tiny_decode_fp32":
+        ctx = np.array([5, 17, 33, 64], dtype=np.int64)
+        return np.ones(4, np.int64), ctx, 2, 2, 64, 16, "fp32", 16
+    if name == "decode_mha_bf16":
+        ctx = rng.integers(128, 4097, size=64).astype(np.int64)
+        return np.ones(64, np.int64), ctx, 32, 32, 128, 16, "bf16", None
+    if name in ("decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64"):
+        u = rng.uniform(math.log(64.0), math.log(32768.0), size=256)
+        ctx = np.clip(np.floor(np.exp(u)), 64, 32768).astype(np.int64)
+        bs = 16 if name.endswith("bs16") else 64
+        return np.ones(256, np.int64), ctx, 32, 8, 128, bs, "bf16", None
+    if name == "prefill_varlen_bf16":
+        comp = rng.choice(3, size=16, p=[0.6, 0.25, 0.15])
+        lo = np.array([10, 1000, 10000])
+        hi = np.array([50, 5000, 20000])
+        lens = np.array([rng.integers(lo[c], hi[c] + 1) for c in comp], dtype=np.int64)
+        return lens.copy(), lens.copy(), 32, 8, 128, 16, "bf16", None
+    if name == "mixed_bf16":
+        dec_ctx = rng.integers(256, 32769, size=200).astype(np.int64)
+        prefix = rng.integers(0, 131073, size=4).astype(np.int64)
+        q = np.concatenate([np.ones(200, np.int64), np.full(4, 512, np.int64)])
+        ctx = np.concatenate([dec_ctx, prefix + 512])
+        return q, ctx, 64, 8, 128, 128, "bf16", None
+    raise KeyError(name)
+
+
+# name -> seed; the GQA block-size pair shares a seed so both runs see identical lengths.
+WORKLOADS = {
+    "tiny_decode_fp32": 1,
+    "decode_mha_bf16": 2,
+    "decode_gqa_bf16_bs16": 3,
+    "decode_gqa_bf16_bs64": 3,
+    "prefill_varlen_bf16": 4,
+    "mixed_bf16": 5,
+}
+
+
+def make_workload(name: str, seed: int | None = None) -> Workload:
+    """Build the integer side of a named synthetic workload (lengths + block table)."""
+    seed = WORKLOADS[name] if seed is None else seed
+    rng = np.random.default_rng(seed)
+    q, ctx, hq, hkv, d, bs, dt, pool = _lengths(name, rng)
+    table, nb = deal_block_table(ctx, bs, rng, pool_blocks=pool)
+    return Workload(name, seed, q, ctx, hq, hkv, d, bs, dt, table, nb)
+
+
+def custom_workload(q_lens, ctx_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                    dtype="bf16", seed=0, spare_blocks=0, name="custom", min_width=1):
+    """A workload with caller-chosen lengths; the block pool is shuffled with ``seed``."""
+    rng = np.random.default_rng(seed)
+    q = np.asarray(q_lens, dtype=np.int64)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    need = int(sum((int(c) + block_size - 1) // block_size for c in ctx))
+    table, nb = deal_block_table(ctx, block_size, rng, pool_blocks=need + spare_blocks,
+                                 min_width=min_width)
+    return Workload(name, seed, q, ctx, num_q_heads, num_kv_heads, head_dim, block_size,
+                    dtype, table, nb)
+
+
+def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinels=True):
+    """Draw tensor values for a workload with a seeded torch generator.
+
+    Returns a dict of torch tensors on ``device``:
+      q      [T, Hq, D]           new queries, packed in sequence order
+      k_new  [T, Hkv, D]          new keys for the same packed tokens
+      v_new  [T, Hkv, D]
+      k_pages, v_pages [NB, Hkv, bs, D]  the pool, holding the cached prefix of every sequence
+    Values are N(0,1) drawn in fp32, then rounded to bf16 (round to nearest even) for bf16
+    workloads. With ``nan_sentinels`` every slot that holds no cached key -- unused blocks, the
+    tail of each sequence's last block, and the slots this step's new tokens will be written
+    to -- is NaN, so a kernel that reads any of them, or skips a write, cannot go unnoticed.
+    """
+    import torch
+    seed = w.seed if seed is None else seed
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T, hq, hkv, d, bs, nb = w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim, \
+        w.block_size, w.num_blocks
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(dt)
+
+    q = draw(T, hq, d)
+    k_new = draw(T, hkv, d)
+    v_new = draw(T, hkv, d)
+    k_pages = draw(nb, hkv, bs, d)
+    v_pages = draw(nb, hkv, bs, d)
+    if nan_sentinels:
+        valid = np.zeros((nb, bs), dtype=bool)
+        for s in range(w.num_seqs):
+            prefix = int(w.ctx_lens[s] - w.q_lens[s])      # slots already cached
+            nblk = (int(w.ctx_lens[s]) + bs - 1) // bs
+            for j in range(nblk):
+                b = int(w.block_table[s, j])
+                lo, hi = j * bs, min((j + 1) * bs, prefix)
+                if hi > lo:
+                    valid[b, : hi - lo] = True
+        mask = torch.from_numpy(~valid).to(device)
+        # [NB, bs] mask over the [NB, bs] leading dims of the (block, slot, head, dim) view
+        k_pages.transpose(1, 2)[mask] = float("nan")
+        v_pages.transpose(1, 2)[mask] = float("nan")
+    return dict(q=q, k_new=k_new, v_new=v_new, k_pages=k_pages, v_pages=v_pages)

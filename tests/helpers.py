@@ -1,0 +1,46 @@
+"""Small test helpers: tensor <-> numpy conversion and tolerance checks (no method arithmetic)."""
+from __future__ import annotations
+
+import numpy as np
+
+# Attention outputs in bf16 (bf16 inputs, fp32 accumulation) versus the fp64 oracle.
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+# fp32 inputs: a reading (only the bf16 bounds are stated); derived in the design doc.
+FP32_MAX_ABS = 1e-4
+FP32_MEAN_ABS = 1e-5
+
+
+def to_np(t):
+    """torch tensor (any float dtype, any device) -> fp64 numpy (exact for bf16/fp32)."""
+    import torch
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def to_np_raw(t):
+    """torch tensor -> numpy holding the same bits (bf16 as uint16) for bit-exact comparisons."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def tolerance(dtype: str):
+    return (BF16_MAX_ABS, BF16_MEAN_ABS) if dtype == "bf16" else (FP32_MAX_ABS, FP32_MEAN_ABS)
+
+
+def check_close(got, ref, dtype, what=""):
+    """Assert max-abs and mean-abs error bounds over the finite reference entries."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    sel = ~np.isnan(ref)
+    assert sel.any(), f"{what}: nothing to compare"
+    assert np.all(np.isfinite(got[sel])), f"{what}: non-finite output"
+    err = np.abs(got[sel] - ref[sel])
+    mx, mean = tolerance(dtype)
+    assert err.max() <= mx, f"{what}: max-abs {err.max():.3e} > {mx}"
+    assert err.mean() <= mean, f"{what}: mean-abs {err.mean():.3e} > {mean}"
+    return float(err.max()), float(err.mean())

@@ -1,0 +1,161 @@
+"""Pins for the cache-write oracle and the task-table oracle. CPU only."""
+import itertools
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as oa
+from oracle import cache as oc
+from oracle import task_table as ot
+from tests.helpers import to_np
+
+
+# ---------------------------------------------------------------- reshape_and_cache
+def test_scatter_round_trip_and_sentinels():
+    w = synth.custom_workload([3, 1, 20], [40, 17, 20], 4, 2, 64, 16, seed=21, spare_blocks=4)
+    v = {k: to_np(t) for k, t in synth.make_values(w, nan_sentinels=True).items()}
+    kp, vp = oc.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"],
+                                  w.block_table, w.q_lens, w.ctx_lens)
+    cu = oa.pack_lengths(w.q_lens)
+    changed = 0
+    for s in range(w.num_seqs):
+        ctx, ql = int(w.ctx_lens[s]), int(w.q_lens[s])
+        K, V = oa.gather_kv(kp, vp, w.block_table[s], ctx, 16)
+        # gather after write returns exactly the new rows at positions P .. ctx-1
+        assert np.array_equal(K[ctx - ql:], v["k_new"][cu[s]:cu[s + 1]])
+        assert np.array_equal(V[ctx - ql:], v["v_new"][cu[s]:cu[s + 1]])
+        # and the cached prefix is untouched
+        K0, V0 = oa.gather_kv(v["k_pages"], v["v_pages"], w.block_table[s], ctx - ql, 16)
+        assert np.array_equal(K[:ctx - ql], K0) and np.array_equal(V[:ctx - ql], V0)
+        changed += ql
+    # exactly T*Hkv*D elements changed per tensor (the NaN sentinels they replaced)
+    diff = ~((kp == v["k_pages"]) | (np.isnan(kp) & np.isnan(v["k_pages"])))
+    assert diff.sum() == changed * 2 * 64
+    # every slot outside the written ones keeps its previous content (NaN stays NaN)
+    assert np.isnan(kp).sum() == np.isnan(v["k_pages"]).sum() - changed * 2 * 64
+
+
+def test_scatter_never_touches_foreign_blocks():
+    w = synth.custom_workload([1, 1], [16, 33], 2, 1, 64, 16, seed=22)
+    v = {k: to_np(t) for k, t in synth.make_values(w, nan_sentinels=False).items()}
+    kp, _ = oc.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"],
+                                 w.block_table, w.q_lens, w.ctx_lens)
+    own = {0: {int(w.block_table[0, 0])}, 1: set(int(b) for b in w.block_table[1, :3])}
+    touched = {b for b in range(w.num_blocks) if not np.array_equal(kp[b], v["k_pages"][b])}
+    # seq 0 writes slot 15 of its only block; seq 1 writes slot 0 of its third block
+    assert touched == {int(w.block_table[0, 0]), int(w.block_table[1, 2])}
+    assert touched <= own[0] | own[1]
+
+
+# ---------------------------------------------------------------- task table
+def P(**kw):
+    base = dict(num_q_heads=2, num_kv_heads=1, head_dim=64, block_size=16, dec_split=64,
+                pf_q_tile=2, pf_kv_split=0, num_workers=2)
+    base.update(kw)
+    return ot.Params(**base)
+
+
+def test_hand_derived_table():
+    """One decode sequence (ctx 100) and one 3-row prefill (ctx 3), Hq=2, Hkv=1 (G=2),
+    dec_split 64, pf_q_tile 2, no prefill key split. Derived by hand:
+      decode seq 0, kv head 0: splits [0,64) and [64,100); 2 splits -> combine, slots 0..3;
+        loads 64*2 = 128 and 36*2 = 72
+      prefill seq 1 (P = 0), head h, rows [0,2): keys visible 1 + 2 = 3; rows [2,3): 3
+    Emission order: d0(128), d1(72), h0r0(3), h0r2(3), h1r0(3), h1r2(3) -- already sorted."""
+    tasks, comb, npart, loads, bal = ot.build_task_table(P(), [0, 1, 4], [100, 3])
+    assert tasks.tolist() == [
+        [0, 0, 0, 0, 1, 0, 64, 0],
+        [0, 0, 0, 0, 1, 64, 100, 2],
+        [1, 1, 0, 0, 2, 0, 2, -1],
+        [1, 1, 0, 2, 1, 0, 3, -1],
+        [1, 1, 1, 0, 2, 0, 2, -1],
+        [1, 1, 1, 2, 1, 0, 3, -1]]
+    assert loads.tolist() == [128, 72, 3, 3, 3, 3]
+    assert comb.tolist() == [[0, 0, 1, 0, 2, 0, 2, 0]]
+    assert npart == 4
+    # modulo: worker0 128+3+3 = 134, worker1 72+3+3 = 78
+    assert bal["modulo"] == pytest.approx(78 / 134)
+    # snake: round0 -> w0 128, w1 72; round1 -> w1 3, w0 3; round2 -> w0 3, w1 3
+    assert bal["snake"] == pytest.approx(78 / 134)
+
+
+def test_balance_examples():
+    """Four equal-shape decode tasks with loads 4,3,2,1 (x G) on two workers:
+    modulo deals w0 = 4+2, w1 = 3+1; snake deals w0 = 4+1, w1 = 3+2."""
+    p = ot.Params(1, 1, 64, 16, dec_split=256, num_workers=2)   # one split per sequence
+    tasks, comb, npart, loads, bal = ot.build_task_table(p, [0, 1, 2, 3, 4], [256, 192, 128, 64])
+    assert loads.tolist() == [256, 192, 128, 64]
+    assert bal["modulo"] == pytest.approx((192 + 64) / (256 + 128))
+    assert bal["snake"] == pytest.approx(1.0)
+
+
+def test_stable_descending_order_with_ties():
+    p = P(num_q_heads=4, num_kv_heads=2, pf_q_tile=4)
+    tasks, _, _, loads, _ = ot.build_task_table(p, [0, 1, 2, 6], [64, 64, 10])
+    assert np.all(np.diff(loads) <= 0)
+    for a, b, la, lb in zip(tasks[:-1], tasks[1:], loads[:-1], loads[1:]):
+        if la == lb:   # ties keep emission order: (seq, head, q_row0, kv0) ascending
+            assert (a[1], a[2], a[3], a[5]) < (b[1], b[2], b[3], b[5])
+
+
+def coverage(p, cu, ctx, tasks):
+    """Count how often each (seq, query head, row, key) pair is covered by the tasks."""
+    G = p.num_q_heads // p.num_kv_heads
+    cnt = {}
+    for kind, s, head, r0, rows, kv0, kv1, _ in tasks.tolist():
+        heads = range(head * G, head * G + G) if kind == 0 else [head]
+        P_ = ctx[s] - (cu[s + 1] - cu[s])
+        for h, i in itertools.product(heads, range(r0, r0 + rows)):
+            for j in range(kv0, min(kv1, P_ + i + 1)):
+                cnt[(s, h, i, j)] = cnt.get((s, h, i, j), 0) + 1
+    return cnt
+
+
+@pytest.mark.parametrize("pf_kv_split,pf_q_tile,dec_split", [(0, 3, 64), (64, 5, 128), (128, 128, 64)])
+def test_coverage_and_load_identities(pf_kv_split, pf_q_tile, dec_split):
+    rng = np.random.default_rng(pf_kv_split + pf_q_tile)
+    q_lens = [1, 7, 1, 19, 1, 2]
+    ctx = [int(rng.integers(1, 300)) if q == 1 else q + int(rng.integers(0, 200)) for q in q_lens]
+    cu = oa.pack_lengths(q_lens).tolist()
+    p = P(num_q_heads=4, num_kv_heads=2, pf_q_tile=pf_q_tile, pf_kv_split=pf_kv_split,
+          dec_split=dec_split, num_workers=3)
+    tasks, comb, npart, loads, _ = ot.build_task_table(p, cu, ctx)
+    cnt = coverage(p, cu, ctx, tasks)
+    expect = {(s, h, i, j) for s in range(len(q_lens)) for h in range(4)
+              for i in range(q_lens[s]) for j in range(ctx[s] - q_lens[s] + i + 1)}
+    assert set(cnt) == expect and all(v == 1 for v in cnt.values())
+    # load identities: decode = sum ctx * Hq ; prefill = Hq * sum_i (P + i + 1)
+    dec = sum(l for t, l in zip(tasks.tolist(), loads) if t[0] == 0)
+    pre = sum(l for t, l in zip(tasks.tolist(), loads) if t[0] == 1)
+    assert dec == sum(c * 4 for q, c in zip(q_lens, ctx) if q == 1)
+    assert pre == sum(4 * sum(c - q + i + 1 for i in range(q)) for q, c in zip(q_lens, ctx) if q > 1)
+    # every task has at least one unmasked pair
+    assert np.all(loads > 0)
+    # partial rows: each used exactly once, all below num_partials, consistent with combines
+    used = []
+    for kind, s, head, r0, rows, kv0, kv1, part in tasks.tolist():
+        if part >= 0:
+            used += list(range(part, part + (2 if kind == 0 else rows)))
+    assert sorted(used) == list(range(npart))
+    assert npart == sum(c[2] * c[4] * c[6] for c in comb.tolist())
+
+
+def test_validation_codes():
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(block_size=12), [0, 1], [5])      # page size 12: rejected
+    assert e.value.code == ot.ERR_BLOCK_SIZE
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(), [0, 2, 2], [5, 5])             # empty sequence
+    assert e.value.code == ot.ERR_INPUT
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(), [0, 4], [3])                   # context shorter than rows
+    assert e.value.code == ot.ERR_INPUT
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(num_q_heads=3, num_kv_heads=2), [0, 1], [3])
+    assert e.value.code == ot.ERR_SHAPE
+
+
+def test_empty_batch():
+    tasks, comb, npart, loads, bal = ot.build_task_table(P(), [0], [])
+    assert tasks.shape == (0, 8) and comb.shape == (0, 8) and npart == 0
