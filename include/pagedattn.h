@@ -1,0 +1,215 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged, variable-length attention library
+ * (libpagedattn.so).
+ *
+ * What is computed. Attention over a block-paged KV cache for packed variable-length
+ * sequences: queries of all sequences are packed back to back and split by cumulative offsets
+ * (cann-recipes-infer Paged KV Cache / Packed Sequence page, section 2.3); keys and values live
+ * in fixed-size pages addressed through a per-sequence int32 page table (same page, sections
+ * 2.2 and 3.1); the operator takes packed q, the pages, the offsets and the page table and runs
+ * causal attention (same page, section 3.3). One task-table-driven kernel family serves decode
+ * and prefill alike (XY-Serve page, section 2.2, "Meta-Attention": GEMM-Softmax-GEMM that does
+ * not distinguish prefill, decode or verify), fed by a load-sorted task table (XY-Serve page,
+ * sections 2.2 and 4.4, Dynamic Decomposer and task reorder).
+ *
+ * Conventions shared by every entry point.
+ *   Layouts (row-major, contiguous, element type given by `dtype`):
+ *     q, out            [num_tokens, Hq, D]           packed in sequence order
+ *     k_new, v_new      [num_tokens, Hkv, D]
+ *     k_pages, v_pages  [num_blocks, Hkv, block_size, D]  two separate pools
+ *     block_table       int32 [num_seqs, max_blocks_per_seq]; entry j of sequence s is the
+ *                       physical block holding keys j*block_size .. (j+1)*block_size-1;
+ *                       entries past ceil(context_lens[s]/block_size) are never read (-1 is
+ *                       the customary filler)
+ *     cu_seqlens_q      int32 [num_seqs+1], cu[0] = 0, strictly increasing
+ *     context_lens      int32 [num_seqs]: keys visible after this step's cache writes, so the
+ *                       cached prefix of sequence s is P_s = context_lens[s] - q_len_s >= 0
+ *   Causality: query row i of sequence s sits at position P_s + i and sees keys 0 .. P_s + i.
+ *   Grouped-query heads: query head h reads kv head h / (Hq / Hkv).
+ *   Softmax scale: the `scale` argument (callers usually pass 1/sqrt(D)).
+ *   Types: dtype PA_BF16 (bf16 in/out, fp32 accumulation) or PA_FP32. head_dim D in {64, 128};
+ *     block_size a power of two in [16, 256] (the cann-recipes-infer page, section 5.3, rejects
+ *     page sizes that are not powers of two >= 16); Hq/Hkv <= 16.
+ *   Memory: the caller owns every buffer. Functions that take `stream` only enqueue work on that
+ *     HIP stream (hipStream_t passed as void*, NULL = default stream): they never allocate,
+ *     free or synchronise device memory. Device pointers must stay valid until the enqueued work
+ *     completes. The cache write must be enqueued before the attention that reads it, on the
+ *     same stream (or with an event between streams).
+ *   Trust: launchers check scalar arguments only. Device-resident data (page ids, lengths,
+ *     offsets, task records) is trusted: ids outside [0, num_blocks) or task records that did
+ *     not come from build_task_table with the same parameters are undefined behaviour, as an
+ *     out-of-range page is on the pages (cann-recipes-infer page, section 4.4).
+ *   Errors: every function returns PA_OK (0) or a negative PA_ERR_* code and sets a
+ *     thread-local message readable with pa_last_error(). Nothing aborts; no exception crosses
+ *     the ABI.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,       /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,      /* head counts, head_dim or tiling parameters not supported */
+  PA_ERR_BLOCK_SIZE = -3, /* block_size not a power of two in [16, 256] */
+  PA_ERR_DTYPE = -4,      /* dtype not supported by this entry point */
+  PA_ERR_CAPACITY = -5,   /* caller buffer too small; required counts are still reported */
+  PA_ERR_INPUT = -6,      /* bad lengths or offsets (host-checked copies only) */
+  PA_ERR_HIP = -7         /* a HIP call or kernel launch failed; see pa_last_error() */
+};
+
+enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 };
+
+enum pa_task_kind { PA_TASK_DECODE = 0, PA_TASK_PREFILL = 1 };
+
+/* One unit of attention work (8 x int32 = 32 bytes).
+ *   kind    PA_TASK_DECODE: the single query row of sequence `seq`, all Hq/Hkv query heads of
+ *           kv head `head`, keys [kv0, kv1).
+ *           PA_TASK_PREFILL: query rows [q_row0, q_row0 + q_rows) (relative to the sequence's
+ *           first packed row) of query head `head`, keys [kv0, kv1) minus the causal mask.
+ *   partial -1: the task sees all keys its rows need and writes `out` directly.
+ *           >= 0: first workspace row of this task's partial result (one row per
+ *           (query row, head) pair it covers); split_combine merges the partials. */
+typedef struct pa_task {
+  int32_t kind, seq, head, q_row0, q_rows, kv0, kv1, partial;
+} pa_task;
+
+/* One merge of split partials into `out` (8 x int32).
+ *   Rows q_row0 .. q_row0+q_rows-1 of sequence `seq`, query heads head .. head+heads-1.
+ *   The partial row of split k, query row i, head j is
+ *   first_slot + k*q_rows*heads + i*heads + j. */
+typedef struct pa_combine {
+  int32_t seq, q_row0, q_rows, head, heads, first_slot, n_slots, reserved;
+} pa_combine;
+
+/* Decomposition parameters.
+ *   dec_split     keys per decode task; positive multiple of 64
+ *   pf_q_tile     query rows per prefill task; 1..128
+ *   pf_kv_split   keys per prefill task along the key axis; 0 = whole visible range, else a
+ *                 positive multiple of 64
+ *   num_workers   workers assumed by the balance report (e.g. CUs x resident workgroups)
+ *   decode_weight integer multiplier of decode-task loads (>= 1), to weigh bandwidth-bound
+ *                 decode tasks against compute-bound prefill tiles in mixed batches */
+typedef struct pa_params {
+  int32_t num_q_heads, num_kv_heads, head_dim, block_size;
+  int32_t dec_split, pf_q_tile, pf_kv_split, num_workers;
+  int32_t decode_weight, reserved[3];
+} pa_params;
+
+/* ABI version of the loaded library (PA_ABI_VERSION when headers and library match). */
+int pa_abi_version(void);
+
+/* Message describing the last error on the calling thread ("" if none). Never NULL; valid
+ * until the next call into the library on the same thread. */
+const char* pa_last_error(void);
+
+/* Packing (cann-recipes-infer page, section 2.3): per-sequence lengths (host, int32 [n], each
+ * >= 1) -> cumulative offsets cu (host, int32 [n+1], cu[0] = 0). PA_ERR_INPUT if a length is
+ * < 1 or the total overflows int32; PA_ERR_NULL for NULL pointers with n > 0 (cu is always
+ * required). Host only, no HIP calls. */
+int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu_seqlens);
+
+/* Dynamic Decomposer (XY-Serve page, sections 2.2 and 4.4): build the load-sorted task table
+ * for one step, on the host, from host copies of cu_seqlens_q [num_seqs+1] and
+ * context_lens [num_seqs].
+ *   Decode sequences (q_len 1) become ceil(ctx/dec_split) key splits per kv head; longer
+ *   sequences become causal query tiles of pf_q_tile rows per query head, each split along its
+ *   visible keys by pf_kv_split. A task's load is its unmasked (row, key) pairs times the heads
+ *   it covers (times decode_weight for decode tasks); tasks are stably sorted by load,
+ *   descending. Partial rows are numbered in emission order (sequence, head, tile, split);
+ *   groups with more than one split get one combine record each.
+ *   Outputs: tasks [tasks_cap], combines [combines_cap] (both caller-owned host buffers);
+ *   *num_tasks, *num_combines, *num_partials always receive the required counts, so a call
+ *   with capacity 0 sizes the buffers (then PA_ERR_CAPACITY). balance, if non-NULL, receives
+ *   {min/max of per-worker load sums when the sorted tasks are dealt in a snake order,
+ *    the same when dealt by i % num_workers} (XY-Serve page, section 4.4, load-balance report).
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (heads or tiling parameters), PA_ERR_BLOCK_SIZE,
+ *   PA_ERR_INPUT (cu[0] != 0, a q_len < 1, a context shorter than its rows),
+ *   PA_ERR_CAPACITY. Pure, deterministic, thread-safe, no HIP calls. */
+int build_task_table(const pa_params* params, const int32_t* cu_seqlens_q_host,
+                     const int32_t* context_lens_host, int32_t num_seqs, pa_task* tasks,
+                     int32_t tasks_cap, int32_t* num_tasks, pa_combine* combines,
+                     int32_t combines_cap, int32_t* num_combines, int32_t* num_partials,
+                     double* balance);
+
+/* Workspace bytes for `num_partials` partial rows of head_dim D (fp32 accumulator row plus
+ * running max and sum), rounded up to 256 bytes. 0 when num_partials <= 0. */
+size_t pa_workspace_bytes(int32_t num_partials, int32_t head_dim);
+
+/* Write this step's new K/V rows into their pages (cann-recipes-infer page, sections 3.2 and
+ * 5.2: new tokens' keys are copied into the pages the table assigns; ATB page, KV reuse: a new
+ * turn appends to the sequence's blocks). Packed token t of sequence s (row i = t - cu[s]) is
+ * copied bit for bit to slot (P_s + i) % block_size of block
+ * block_table[s][(P_s + i) / block_size], for K and V, every kv head.
+ *   Device pointers: k_new, v_new, k_pages, v_pages, block_table, cu_seqlens_q, context_lens.
+ *   num_tokens must equal cu_seqlens_q[num_seqs] (not checked on the device). Two tokens
+ *   mapped to one slot is malformed input (undefined which write wins).
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_tokens/num_seqs < 0, Hkv < 1, D not 64/128),
+ *   PA_ERR_BLOCK_SIZE, PA_ERR_DTYPE, PA_ERR_HIP. num_tokens == 0 is a no-op. */
+int reshape_and_cache(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
+/* Decode attention: one query token per sequence (MindIE page, "Continuous Batching": each
+ * step decodes one token per request), q [num_seqs, Hq, D] -> out [num_seqs, Hq, D].
+ * Runs the decode tasks of a table built with cu_seqlens_q = 0, 1, ..., num_seqs (copied to
+ * the device by the caller: tasks_dev [num_tasks], combines_dev [num_combines]), then merges
+ * split partials with a log-sum-exp combine. Each KV page is read once for all query heads of
+ * its kv head.
+ *   workspace: device buffer of at least pa_workspace_bytes(num_partials, D) bytes
+ *   (may be NULL when num_combines == 0).
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (Hq % Hkv, Hq/Hkv > 16, D), PA_ERR_BLOCK_SIZE,
+ *   PA_ERR_DTYPE, PA_ERR_CAPACITY (workspace too small for the combines' partial rows),
+ *   PA_ERR_HIP. */
+int paged_attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      int32_t dtype, const pa_task* tasks_dev, int32_t num_tasks,
+                      const pa_combine* combines_dev, int32_t num_combines,
+                      int32_t num_partials, void* workspace, size_t workspace_bytes, void* out,
+                      void* stream);
+
+/* Packed variable-length causal attention over paged prefixes, any mix of decode rows and
+ * prefill chunks in one launch (cann-recipes-infer page, section 3.3: paged_attention(q_packed,
+ * kv_pages, cu_seqlens, page_table, is_causal=True); MindIE page, "Prefill Chunking": chunks
+ * over an already cached prefix). q [num_tokens, Hq, D] -> out [num_tokens, Hq, D].
+ * Decode tasks run the split-K decode path, prefill tasks the bf16 MFMA tile path, both inside
+ * one grid in table order; then split partials are merged.
+ *   dtype must be PA_BF16 (the prefill path runs on bf16 MFMA).
+ *   Errors as paged_attn_decode, plus PA_ERR_SHAPE for num_tokens < num_seqs and
+ *   PA_ERR_DTYPE for any dtype other than PA_BF16. */
+int paged_attn_varlen_prefill(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float scale, int32_t dtype, const pa_task* tasks_dev,
+                              int32_t num_tasks, const pa_combine* combines_dev,
+                              int32_t num_combines, int32_t num_partials, void* workspace,
+                              size_t workspace_bytes, void* out, void* stream);
+
+/* Debug check of a host copy of a block table (cann-recipes-infer page, section 4.4, first
+ * check: page ids inside [0, max_pages)): every entry a sequence needs,
+ * j < ceil(context_lens[s]/block_size), must lie in [0, num_blocks), and no physical block may
+ * be claimed twice. Returns PA_OK or PA_ERR_INPUT (message names the first bad entry),
+ * PA_ERR_NULL, PA_ERR_SHAPE (ceil(ctx/block_size) > max_blocks_per_seq). Host only. */
+int pa_validate_block_table(const int32_t* block_table_host, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens_host, int32_t num_seqs,
+                            int32_t num_blocks, int32_t block_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

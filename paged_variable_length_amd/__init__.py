@@ -1,0 +1,266 @@
+"""Paged, variable-length attention for MI355X (gfx950): Python binding of libpagedattn.so.
+
+The functions here carry the names of the C ABI (include/pagedattn.h) and only marshal
+arguments: torch tensors are used for device memory and streams, every step of the path runs
+in the library's HIP kernels or its host C++. Nothing here computes attention, and nothing
+falls back to a CPU path: a missing library raises.
+
+    pack_seqlens             per-sequence lengths -> cu_seqlens (host)
+    build_task_table         Dynamic Decomposer: load-sorted task table (host)
+    workspace_bytes          bytes of the split-partial workspace
+    reshape_and_cache        write new K/V rows into their pages (device)
+    paged_attn_decode        decode attention, one query token per sequence (device)
+    paged_attn_varlen_prefill  packed causal attention, any mix of decode and prefill (device)
+    validate_block_table     debug check of a host block table
+    StepPlan                 convenience: a built table copied to the device with its workspace
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _abi
+from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL, PagedAttnError,  # noqa: F401
+                   PaCombine, PaParams, PaTask, check, lib)
+
+__all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
+           "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
+           "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32"]
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def pack_seqlens(lengths) -> np.ndarray:
+    """Host lengths [n] -> cu_seqlens int32 [n+1] (library call)."""
+    ln = _i32(lengths)
+    cu = np.zeros(ln.shape[0] + 1, dtype=np.int32)
+    check(lib().pa_pack_seqlens(_ptr(ln), ln.shape[0], _ptr(cu)), "pa_pack_seqlens")
+    return cu
+
+
+def make_params(num_q_heads, num_kv_heads, head_dim, block_size, dec_split=512, pf_q_tile=128,
+                pf_kv_split=0, num_workers=256, decode_weight=1) -> PaParams:
+    return PaParams(num_q_heads, num_kv_heads, head_dim, block_size, dec_split, pf_q_tile,
+                    pf_kv_split, num_workers, decode_weight, (ctypes.c_int32 * 3)(0, 0, 0))
+
+
+@dataclass
+class TaskTable:
+    tasks: np.ndarray        # int32 [n, 8]
+    combines: np.ndarray     # int32 [m, 8]
+    num_partials: int
+    balance_snake: float
+    balance_modulo: float
+
+
+def build_task_table(params: PaParams, cu_seqlens_q, context_lens) -> TaskTable:
+    """Host task table (library call); two-call sizing through PA_ERR_CAPACITY."""
+    L = lib()
+    cu = _i32(cu_seqlens_q)
+    ctx = _i32(context_lens)
+    n = ctx.shape[0]
+    nt, nc, npart = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    bal = (ctypes.c_double * 2)()
+    rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, None, 0,
+                            ctypes.byref(nt), None, 0, ctypes.byref(nc), ctypes.byref(npart), bal)
+    if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
+        check(rc, "build_task_table")
+    tasks = np.zeros((nt.value, 8), dtype=np.int32)
+    comb = np.zeros((nc.value, 8), dtype=np.int32)
+    rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n,
+                            tasks.ctypes.data_as(ctypes.POINTER(PaTask)), nt.value,
+                            ctypes.byref(nt), comb.ctypes.data_as(ctypes.POINTER(PaCombine)),
+                            nc.value, ctypes.byref(nc), ctypes.byref(npart), bal)
+    check(rc, "build_task_table")
+    return TaskTable(tasks, comb, npart.value, bal[0], bal[1])
+
+
+def workspace_bytes(num_partials: int, head_dim: int) -> int:
+    return int(lib().pa_workspace_bytes(int(num_partials), int(head_dim)))
+
+
+def validate_block_table(block_table, context_lens, num_blocks, block_size):
+    bt = _i32(block_table)
+    ctx = _i32(context_lens)
+    check(lib().pa_validate_block_table(_ptr(bt), bt.shape[1] if bt.ndim == 2 else 0, _ptr(ctx),
+                                        ctx.shape[0], int(num_blocks), int(block_size)),
+          "pa_validate_block_table")
+
+
+# ------------------------------------------------------------------ device-side marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_FP32
+    raise PagedAttnError(_abi.PA_ERR_DTYPE, "binding", f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    """Check a tensor is a contiguous GPU tensor (a kernel given a host pointer would fault)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def reshape_and_cache(k_new, v_new, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
+                      stream=None):
+    """Write packed new K/V rows [T, Hkv, D] into pages [NB, Hkv, bs, D] (library kernel)."""
+    torch = _torch()
+    T, hkv, d = k_new.shape
+    nb, hkv2, bs, d2 = k_pages.shape
+    if (hkv, d) != (hkv2, d2) or v_new.shape != k_new.shape or v_pages.shape != k_pages.shape:
+        raise ValueError("k/v shapes disagree")
+    if not (k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype):
+        raise ValueError("k/v dtypes disagree")
+    n = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != n or cu_seqlens_q.shape[0] != n + 1:
+        raise ValueError("block_table / cu_seqlens_q / context_lens sizes disagree")
+    args = [_dev(k_new, "k_new", ndim=3), _dev(v_new, "v_new", ndim=3),
+            _dev(k_pages, "k_pages", ndim=4), _dev(v_pages, "v_pages", ndim=4),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32), n, T, nb, hkv, d, bs,
+            _dtype_code(k_new), _stream(stream)]
+    check(lib().reshape_and_cache(*args), "reshape_and_cache")
+
+
+def _attn_common(q, k_pages, v_pages, block_table, context_lens, out):
+    torch = _torch()
+    if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
+        raise ValueError("k_pages and v_pages must both be [NB, Hkv, bs, D]")
+    if q.dim() != 3 or out.shape != q.shape or q.dtype != out.dtype:
+        raise ValueError("q and out must both be [T, Hq, D] of one dtype")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise ValueError("q and pages must share a dtype")
+    if q.shape[2] != k_pages.shape[3]:
+        raise ValueError("head_dim of q and pages differ")
+    n = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != n:
+        raise ValueError("block_table must be [num_seqs, max_blocks]")
+    return [_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1]]
+
+
+def _table_args(tasks_dev, combines_dev, num_partials, workspace):
+    torch = _torch()
+    _dev(tasks_dev, "tasks_dev", torch.int32, 2)
+    if combines_dev.shape[0] > 0:
+        _dev(combines_dev, "combines_dev", torch.int32, 2)
+    ws = None
+    wsb = 0
+    if workspace is not None and workspace.numel() > 0:
+        ws = _dev(workspace, "workspace")
+        wsb = workspace.numel() * workspace.element_size()
+    return [ctypes.c_void_p(tasks_dev.data_ptr()), tasks_dev.shape[0],
+            ctypes.c_void_p(combines_dev.data_ptr() if combines_dev.numel() else 0),
+            combines_dev.shape[0], int(num_partials), ws, wsb]
+
+
+def paged_attn_decode(q, k_pages, v_pages, block_table, context_lens, scale, tasks_dev,
+                      combines_dev, num_partials, workspace, out, stream=None):
+    """Decode attention (library kernels). q/out [N, Hq, D]; tasks from a table built with
+    cu_seqlens = 0..N, copied to the device as int32 [n, 8]."""
+    torch = _torch()
+    head = _attn_common(q, k_pages, v_pages, block_table, context_lens, out)
+    n, hq, d = q.shape
+    if context_lens.shape[0] != n:
+        raise ValueError("decode takes one query row per sequence")
+    args = head + [_dev(context_lens, "context_lens", torch.int32), n, hq, k_pages.shape[1], d,
+                   k_pages.shape[2], float(scale), _dtype_code(q)] + \
+        _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        [_dev(out, "out"), _stream(stream)]
+    check(lib().paged_attn_decode(*args), "paged_attn_decode")
+
+
+def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
+                              scale, tasks_dev, combines_dev, num_partials, workspace, out,
+                              stream=None):
+    """Packed causal attention over paged prefixes, decode rows and prefill chunks mixed
+    (library kernels). q/out [T, Hq, D]."""
+    torch = _torch()
+    head = _attn_common(q, k_pages, v_pages, block_table, context_lens, out)
+    T, hq, d = q.shape
+    n = context_lens.shape[0]
+    if cu_seqlens_q.shape[0] != n + 1:
+        raise ValueError("cu_seqlens_q must be [num_seqs + 1]")
+    args = head + [_dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                   _dev(context_lens, "context_lens", torch.int32), n, T, hq, k_pages.shape[1],
+                   d, k_pages.shape[2], float(scale), _dtype_code(q)] + \
+        _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        [_dev(out, "out"), _stream(stream)]
+    check(lib().paged_attn_varlen_prefill(*args), "paged_attn_varlen_prefill")
+
+
+class StepPlan:
+    """A task table built on the host for one batch, copied to the device, with its workspace.
+
+    Holds device int32 copies of cu_seqlens, context_lens, the block table and the table, so a
+    caller can launch the step repeatedly. All memory comes from torch's allocator.
+    """
+
+    def __init__(self, q_lens, context_lens, block_table, num_q_heads, num_kv_heads, head_dim,
+                 block_size, device="cuda", **tiling):
+        torch = _torch()
+        self.cu_host = pack_seqlens(q_lens)
+        self.ctx_host = _i32(context_lens)
+        self.params = make_params(num_q_heads, num_kv_heads, head_dim, block_size, **tiling)
+        self.table = build_task_table(self.params, self.cu_host, self.ctx_host)
+        self.head_dim = head_dim
+        self.device = device
+        self.cu = torch.from_numpy(self.cu_host).to(device)
+        self.ctx = torch.from_numpy(self.ctx_host).to(device)
+        self.block_table = torch.from_numpy(_i32(block_table)).to(device)
+        self.tasks = torch.from_numpy(self.table.tasks).to(device)
+        self.combines = torch.from_numpy(self.table.combines).to(device)
+        nbytes = workspace_bytes(self.table.num_partials, head_dim)
+        self.workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
+        self.decode_only = bool(np.all(np.diff(self.cu_host) == 1))
+
+    @property
+    def num_partials(self):
+        return self.table.num_partials
+
+    def write_cache(self, k_new, v_new, k_pages, v_pages, stream=None):
+        reshape_and_cache(k_new, v_new, k_pages, v_pages, self.block_table, self.cu, self.ctx,
+                          stream)
+
+    def decode(self, q, k_pages, v_pages, scale, out, stream=None):
+        paged_attn_decode(q, k_pages, v_pages, self.block_table, self.ctx, scale, self.tasks,
+                          self.combines, self.num_partials, self.workspace, out, stream)
+
+    def varlen(self, q, k_pages, v_pages, scale, out, stream=None):
+        paged_attn_varlen_prefill(q, k_pages, v_pages, self.block_table, self.cu, self.ctx,
+                                  scale, self.tasks, self.combines, self.num_partials,
+                                  self.workspace, out, stream)

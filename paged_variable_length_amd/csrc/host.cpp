@@ -1,0 +1,229 @@
+// Host-side parts of libpagedattn.so: error state, packing, the Dynamic Decomposer's task
+// table, workspace sizing and the block-table debug check. No HIP calls in this file.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "internal.h"
+
+namespace pa {
+
+static thread_local char g_err[512] = "";
+
+int clear_error() {
+  g_err[0] = '\0';
+  return PA_OK;
+}
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace pa
+
+using pa::set_error;
+
+extern "C" int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+extern "C" const char* pa_last_error(void) { return pa::g_err; }
+
+// Packing into cumulative offsets (cann-recipes-infer page, section 2.3).
+extern "C" int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu) {
+  if (!cu || (n > 0 && !lengths)) return set_error(PA_ERR_NULL, "pa_pack_seqlens: NULL pointer");
+  if (n < 0) return set_error(PA_ERR_INPUT, "pa_pack_seqlens: negative count %d", n);
+  int64_t run = 0;
+  cu[0] = 0;
+  for (int32_t s = 0; s < n; ++s) {
+    if (lengths[s] < 1)
+      return set_error(PA_ERR_INPUT, "pa_pack_seqlens: length[%d] = %d < 1", s, lengths[s]);
+    run += lengths[s];
+    if (run > INT32_MAX) return set_error(PA_ERR_INPUT, "pa_pack_seqlens: total overflows int32");
+    cu[s + 1] = static_cast<int32_t>(run);
+  }
+  return pa::clear_error();
+}
+
+namespace {
+
+struct Emitted {
+  int64_t load;
+  pa_task task;
+};
+
+int check_params(const pa_params* p) {
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
+    return set_error(PA_ERR_SHAPE, "query heads (%d) must be a positive multiple of kv heads (%d)",
+                     p->num_q_heads, p->num_kv_heads);
+  if (!pa::block_size_ok(p->block_size))
+    return set_error(PA_ERR_BLOCK_SIZE, "block_size %d is not a power of two in [16, 256]",
+                     p->block_size);
+  if (p->dec_split < pa::kSplitQuantum || p->dec_split % pa::kSplitQuantum)
+    return set_error(PA_ERR_SHAPE, "dec_split %d must be a positive multiple of %d", p->dec_split,
+                     pa::kSplitQuantum);
+  if (p->pf_q_tile < 1 || p->pf_q_tile > pa::kMaxQTile)
+    return set_error(PA_ERR_SHAPE, "pf_q_tile %d must lie in [1, %d]", p->pf_q_tile,
+                     pa::kMaxQTile);
+  if (p->pf_kv_split < 0 || p->pf_kv_split % pa::kSplitQuantum)
+    return set_error(PA_ERR_SHAPE, "pf_kv_split %d must be 0 or a positive multiple of %d",
+                     p->pf_kv_split, pa::kSplitQuantum);
+  if (p->num_workers < 1 || p->decode_weight < 1)
+    return set_error(PA_ERR_SHAPE, "num_workers and decode_weight must be >= 1");
+  return PA_OK;
+}
+
+double ratio(const std::vector<int64_t>& v) {
+  int64_t mx = *std::max_element(v.begin(), v.end());
+  int64_t mn = *std::min_element(v.begin(), v.end());
+  return mx == 0 ? 1.0 : static_cast<double>(mn) / static_cast<double>(mx);
+}
+
+}  // namespace
+
+// Dynamic Decomposer + load-sorted reorder (XY-Serve page, sections 2.2 and 4.4).
+extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int32_t* ctx,
+                                int32_t num_seqs, pa_task* tasks, int32_t tasks_cap,
+                                int32_t* num_tasks, pa_combine* combines, int32_t combines_cap,
+                                int32_t* num_combines, int32_t* num_partials, double* balance) {
+  if (!p || !cu || (num_seqs > 0 && !ctx) || !num_tasks || !num_combines || !num_partials)
+    return set_error(PA_ERR_NULL, "build_task_table: NULL pointer");
+  if (int rc = check_params(p)) return rc;
+  if (num_seqs < 0) return set_error(PA_ERR_INPUT, "num_seqs %d < 0", num_seqs);
+  if (cu[0] != 0) return set_error(PA_ERR_INPUT, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (cu[s + 1] <= cu[s])
+      return set_error(PA_ERR_INPUT, "cu_seqlens must increase strictly (seq %d)", s);
+    if (ctx[s] < cu[s + 1] - cu[s])
+      return set_error(PA_ERR_INPUT, "context_lens[%d] = %d is shorter than its %d query rows",
+                       s, ctx[s], cu[s + 1] - cu[s]);
+  }
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  std::vector<Emitted> em;
+  std::vector<pa_combine> comb;
+  int64_t parts = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ql = cu[s + 1] - cu[s];
+    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
+    if (ql == 1) {
+      // decode: key splits of dec_split per kv head, all G query heads in one task
+      const int32_t nsplit =
+          static_cast<int32_t>((int64_t(ctx[s]) + p->dec_split - 1) / p->dec_split);
+      for (int32_t g = 0; g < p->num_kv_heads; ++g) {
+        int64_t first = -1;
+        if (nsplit > 1) {
+          first = parts;
+          parts += static_cast<int64_t>(nsplit) * G;
+          comb.push_back(pa_combine{s, 0, 1, g * G, G, static_cast<int32_t>(first), nsplit, 0});
+        }
+        for (int32_t k = 0; k < nsplit; ++k) {
+          const int32_t kv0 = k * p->dec_split;
+          const int32_t kv1 = std::min(ctx[s], kv0 + p->dec_split);
+          const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * G) : -1;
+          const int64_t load = int64_t(kv1 - kv0) * G * p->decode_weight;
+          em.push_back(Emitted{load, pa_task{PA_TASK_DECODE, s, g, 0, 1, kv0, kv1, part}});
+        }
+      }
+    } else {
+      // prefill: causal query tiles per query head, each split along its visible keys
+      for (int32_t h = 0; h < p->num_q_heads; ++h) {
+        for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
+          const int32_t rows = std::min(p->pf_q_tile, ql - r0);
+          const int64_t lim = prefix + r0 + rows;  // keys visible to the tile's last row
+          const int64_t split = p->pf_kv_split > 0 ? p->pf_kv_split : lim;
+          const int32_t nsplit = static_cast<int32_t>((lim + split - 1) / split);
+          int64_t first = -1;
+          if (nsplit > 1) {
+            first = parts;
+            parts += static_cast<int64_t>(nsplit) * rows;
+            comb.push_back(pa_combine{s, r0, rows, h, 1, static_cast<int32_t>(first), nsplit, 0});
+          }
+          for (int32_t k = 0; k < nsplit; ++k) {
+            const int64_t kv0 = k * split;
+            const int64_t kv1 = std::min(lim, kv0 + split);
+            int64_t load = 0;
+            for (int32_t i = r0; i < r0 + rows; ++i)
+              load += std::max<int64_t>(0, std::min(kv1, prefix + i + 1) - kv0);
+            const int32_t part =
+                nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * rows) : -1;
+            em.push_back(Emitted{load, pa_task{PA_TASK_PREFILL, s, h, r0, rows,
+                                               static_cast<int32_t>(kv0),
+                                               static_cast<int32_t>(kv1), part}});
+          }
+        }
+      }
+    }
+    if (parts > INT32_MAX || em.size() > size_t(INT32_MAX))
+      return set_error(PA_ERR_SHAPE, "task table exceeds int32 indexing");
+  }
+  // stable sort by load, descending: ties keep emission order
+  std::stable_sort(em.begin(), em.end(),
+                   [](const Emitted& a, const Emitted& b) { return a.load > b.load; });
+  *num_tasks = static_cast<int32_t>(em.size());
+  *num_combines = static_cast<int32_t>(comb.size());
+  *num_partials = static_cast<int32_t>(parts);
+  if (balance) {
+    const int32_t W = p->num_workers;
+    std::vector<int64_t> snake(W, 0), modulo(W, 0);
+    for (size_t i = 0; i < em.size(); ++i) {
+      const size_t rnd = i / W, pos = i % W;
+      snake[rnd % 2 == 0 ? pos : W - 1 - pos] += em[i].load;
+      modulo[i % W] += em[i].load;
+    }
+    balance[0] = ratio(snake);
+    balance[1] = ratio(modulo);
+  }
+  if (static_cast<int64_t>(em.size()) > tasks_cap || static_cast<int64_t>(comb.size()) > combines_cap)
+    return set_error(PA_ERR_CAPACITY, "need %zu tasks (cap %d) and %zu combines (cap %d)",
+                     em.size(), tasks_cap, comb.size(), combines_cap);
+  if (!em.empty() && !tasks) return set_error(PA_ERR_NULL, "build_task_table: tasks is NULL");
+  if (!comb.empty() && !combines)
+    return set_error(PA_ERR_NULL, "build_task_table: combines is NULL");
+  for (size_t i = 0; i < em.size(); ++i) tasks[i] = em[i].task;
+  if (!comb.empty()) std::memcpy(combines, comb.data(), comb.size() * sizeof(pa_combine));
+  return pa::clear_error();
+}
+
+extern "C" size_t pa_workspace_bytes(int32_t num_partials, int32_t head_dim) {
+  if (num_partials <= 0 || head_dim <= 0) return 0;
+  // [num_partials, D] fp32 accumulators, then [num_partials, 2] fp32 (running max, sum);
+  // the second region starts on a 256-byte boundary
+  size_t acc = static_cast<size_t>(num_partials) * head_dim * sizeof(float);
+  acc = (acc + 255) & ~size_t(255);
+  size_t ml = static_cast<size_t>(num_partials) * 2 * sizeof(float);
+  return (acc + ml + 255) & ~size_t(255);
+}
+
+// Debug check of a host block table (cann-recipes-infer page, section 4.4, first check).
+extern "C" int pa_validate_block_table(const int32_t* bt, int32_t width, const int32_t* ctx,
+                                       int32_t num_seqs, int32_t num_blocks, int32_t bs) {
+  if ((num_seqs > 0 && (!bt || !ctx)))
+    return set_error(PA_ERR_NULL, "pa_validate_block_table: NULL pointer");
+  if (!pa::block_size_ok(bs))
+    return set_error(PA_ERR_BLOCK_SIZE, "block_size %d is not a power of two in [16, 256]", bs);
+  if (num_blocks < 0 || width < 0 || num_seqs < 0)
+    return set_error(PA_ERR_SHAPE, "negative size");
+  std::vector<int32_t> owner(static_cast<size_t>(num_blocks), -1);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (ctx[s] < 0) return set_error(PA_ERR_INPUT, "context_lens[%d] = %d < 0", s, ctx[s]);
+    const int32_t need = (ctx[s] + bs - 1) / bs;
+    if (need > width)
+      return set_error(PA_ERR_SHAPE, "seq %d needs %d blocks, table has %d columns", s, need,
+                       width);
+    for (int32_t j = 0; j < need; ++j) {
+      const int32_t b = bt[static_cast<int64_t>(s) * width + j];
+      if (b < 0 || b >= num_blocks)
+        return set_error(PA_ERR_INPUT, "block_table[%d][%d] = %d outside [0, %d)", s, j, b,
+                         num_blocks);
+      if (owner[b] >= 0)
+        return set_error(PA_ERR_INPUT, "physical block %d claimed by seq %d and seq %d", b,
+                         owner[b], s);
+      owner[b] = s;
+    }
+  }
+  return pa::clear_error();
+}

@@ -1,0 +1,187 @@
+"""Host-side checks of libpagedattn.so (no GPU needed): the library loads and exports every
+symbol the header declares, and its host functions -- packing, the task table, workspace
+sizing, block-table validation, argument checks -- agree with the oracle or the header.
+The task table must match the oracle's bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import paged_variable_length_amd as pa
+from paged_variable_length_amd import _abi
+from oracle import task_table as ot
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pagedattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\(", text, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    declared = header_functions()
+    assert declared == set(_abi.EXPORTS), declared ^ set(_abi.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.pa_abi_version() == _abi.ABI_VERSION
+
+
+def test_pack_seqlens_worked_example_and_errors():
+    assert pa.pack_seqlens([128, 64, 256]).tolist() == [0, 128, 192, 448]
+    assert pa.pack_seqlens([]).tolist() == [0]
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.pack_seqlens([3, 0])
+    assert e.value.code == _abi.PA_ERR_INPUT
+    with pytest.raises(pa.PagedAttnError):
+        pa.pack_seqlens([2**30, 2**30, 2**30])
+
+
+def compare_tables(q_lens, ctx, **kw):
+    hq, hkv, d, bs = kw.pop("hq"), kw.pop("hkv"), kw.pop("d", 128), kw.pop("bs")
+    cu = pa.pack_seqlens(q_lens)
+    got = pa.build_task_table(pa.make_params(hq, hkv, d, bs, **kw), cu, ctx)
+    ref_t, ref_c, ref_np, _, ref_bal = ot.build_task_table(ot.Params(hq, hkv, d, bs, **kw), cu, ctx)
+    assert np.array_equal(got.tasks, ref_t)
+    assert np.array_equal(got.combines, ref_c)
+    assert got.num_partials == ref_np
+    assert got.balance_snake == ref_bal["snake"]
+    assert got.balance_modulo == ref_bal["modulo"]
+    return got
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_fp32", "decode_mha_bf16", "decode_gqa_bf16_bs16",
+                                  "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16"])
+def test_task_table_bit_exact_on_workloads(name):
+    w = synth.make_workload(name)
+    tiling = dict(dec_split=512, pf_q_tile=128, pf_kv_split=0 if name != "mixed_bf16" else 8192)
+    compare_tables(w.q_lens, w.ctx_lens, hq=w.num_q_heads, hkv=w.num_kv_heads, d=w.head_dim,
+                   bs=w.block_size, num_workers=512, **tiling)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_task_table_bit_exact_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 12))
+    q = [1 if rng.random() < 0.5 else int(rng.integers(2, 300)) for _ in range(n)]
+    ctx = [qq + int(rng.integers(0, 700)) for qq in q]
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    compare_tables(q, ctx, hq=hq, hkv=hkv, bs=int(rng.choice([16, 32, 64, 128, 256])),
+                   dec_split=64 * int(rng.integers(1, 6)), pf_q_tile=int(rng.integers(1, 129)),
+                   pf_kv_split=64 * int(rng.integers(0, 5)), num_workers=int(rng.integers(1, 40)),
+                   decode_weight=int(rng.integers(1, 4)))
+
+
+def test_task_table_errors_match_oracle():
+    cases = [
+        (dict(hq=2, hkv=1, bs=12), [1], [5], _abi.PA_ERR_BLOCK_SIZE),
+        (dict(hq=2, hkv=1, bs=48), [1], [5], _abi.PA_ERR_BLOCK_SIZE),
+        (dict(hq=3, hkv=2, bs=16), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, dec_split=100), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, pf_q_tile=129), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, pf_kv_split=32), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16), [4], [3], _abi.PA_ERR_INPUT),
+    ]
+    for kw, q, ctx, code in cases:
+        hq, hkv, bs = kw.pop("hq"), kw.pop("hkv"), kw.pop("bs")
+        cu = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+        with pytest.raises(pa.PagedAttnError) as e:
+            pa.build_task_table(pa.make_params(hq, hkv, 64, bs, **kw), cu, ctx)
+        assert e.value.code == code
+        with pytest.raises(ot.TaskTableError) as e2:
+            ot.build_task_table(ot.Params(hq, hkv, 64, bs, **kw), cu, ctx)
+        assert e2.value.code == code
+    # non-increasing offsets are caught by the table builder itself
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.build_task_table(pa.make_params(2, 1, 64, 16), np.array([0, 2, 2], np.int32), [5, 5])
+    assert e.value.code == _abi.PA_ERR_INPUT
+
+
+def test_task_table_capacity_sizing():
+    L = _abi.lib()
+    p = pa.make_params(2, 1, 64, 16, dec_split=64)
+    cu = np.array([0, 1], np.int32)
+    ctx = np.array([200], np.int32)
+    nt, nc, npart = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    P = ctypes.POINTER(ctypes.c_int32)
+    rc = L.build_task_table(ctypes.byref(p), cu.ctypes.data_as(P), ctx.ctypes.data_as(P), 1,
+                            None, 0, ctypes.byref(nt), None, 0, ctypes.byref(nc),
+                            ctypes.byref(npart), None)
+    assert rc == _abi.PA_ERR_CAPACITY
+    assert (nt.value, nc.value, npart.value) == (4, 1, 8)
+
+
+def test_empty_batch_table():
+    t = pa.build_task_table(pa.make_params(2, 1, 64, 16), np.array([0], np.int32),
+                            np.zeros(0, np.int32))
+    assert t.tasks.shape == (0, 8) and t.combines.shape == (0, 8) and t.num_partials == 0
+
+
+def test_workspace_bytes():
+    assert pa.workspace_bytes(0, 128) == 0
+    # 3 rows * 128 floats = 1536 B (already 256-aligned) + 3 * 8 B -> 1560 -> 1792
+    assert pa.workspace_bytes(3, 128) == 1792
+    assert pa.workspace_bytes(1, 64) % 256 == 0 and pa.workspace_bytes(1, 64) >= 256 + 8
+
+
+def test_validate_block_table():
+    w = synth.custom_workload([1, 1], [20, 40], 2, 1, 64, 16, seed=1)
+    pa.validate_block_table(w.block_table, w.ctx_lens, w.num_blocks, 16)
+    bad = w.block_table.copy()
+    bad[1, 1] = w.num_blocks            # out of range
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.validate_block_table(bad, w.ctx_lens, w.num_blocks, 16)
+    assert e.value.code == _abi.PA_ERR_INPUT
+    dup = w.block_table.copy()
+    dup[1, 0] = dup[0, 0]               # one physical block claimed twice
+    with pytest.raises(pa.PagedAttnError):
+        pa.validate_block_table(dup, w.ctx_lens, w.num_blocks, 16)
+    # an entry past a sequence's need is never checked (it is never read)
+    tail = w.block_table.copy()
+    tail[0, 2] = 10**6                 # seq 0 (ctx 20) needs 2 of the 3 columns
+    pa.validate_block_table(tail, w.ctx_lens, w.num_blocks, 16)
+
+
+def test_launcher_scalar_errors_need_no_gpu():
+    """Scalar argument checks run before any HIP call, so bad shapes are reported on the host."""
+    L = _abi.lib()
+    nul = None
+    # block size 12
+    rc = L.reshape_and_cache(nul, nul, nul, nul, nul, 1, nul, nul, 1, 1, 1, 1, 64, 12, 0, nul)
+    assert rc == _abi.PA_ERR_BLOCK_SIZE
+    # head_dim 96
+    rc = L.reshape_and_cache(nul, nul, nul, nul, nul, 1, nul, nul, 1, 1, 1, 1, 96, 16, 0, nul)
+    assert rc == _abi.PA_ERR_SHAPE
+    # zero tokens: no-op, no pointer needed
+    rc = L.reshape_and_cache(nul, nul, nul, nul, nul, 1, nul, nul, 1, 0, 1, 1, 64, 16, 0, nul)
+    assert rc == _abi.PA_OK
+    args = lambda hq, hkv, d, bs, dt, ncomb=0, ws=None, wsb=0: [  # noqa: E731
+        nul, nul, nul, nul, 1, nul, 1, hq, hkv, d, bs, 0.1, dt, nul, 1, nul, ncomb, 8, ws, wsb,
+        nul, nul]
+    assert L.paged_attn_decode(*args(3, 2, 64, 16, 0)) == _abi.PA_ERR_SHAPE
+    assert L.paged_attn_decode(*args(34, 1, 64, 16, 0)) == _abi.PA_ERR_SHAPE     # G > 16
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 7)) == _abi.PA_ERR_DTYPE
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0, 1, None, 0)) == _abi.PA_ERR_NULL
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0, 1, ctypes.c_void_p(16), 8)) == \
+        _abi.PA_ERR_CAPACITY
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0)) == _abi.PA_ERR_NULL       # NULL q
+    assert b"NULL" in L.pa_last_error()
+    v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, nul, 0, 0, nul, 0,
+         nul, nul]
+    assert L.paged_attn_varlen_prefill(*v) == _abi.PA_ERR_DTYPE                  # fp32 prefill
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    pages = torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16)
+    i = torch.zeros(2, 1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.reshape_and_cache(k, k, pages, pages, i, torch.zeros(3, dtype=torch.int32),
+                             torch.zeros(2, dtype=torch.int32))
