@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged, variable-length attention path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: cu_seqlens packing and the
+load-sorted task table on the host (C++), the table's copy to the device, reshape_and_cache of
+the step's new K/V, the attention launch (decode splits and/or prefill tiles) and the split
+combine. Inputs are resident in HBM before timing starts; the host table build of step k+1
+overlaps the GPU work of step k (two table slots, reused only after their event completes).
+
+Headline (`value`): decode KV GB/s on the 64-sequence MHA decode batch (Hq = Hkv = 32, D 128,
+16-token blocks, contexts U[128, 4096]): algorithmic bytes per step (every visible K/V row, q,
+out, the block-table entries read) over the measured step time. Secondary workloads in the same
+JSON line: GQA decode at block sizes 16 and 64, the packed varlen causal prefill (TFLOP/s) and
+the mixed unified step (both). `roofline` covers the attention launch of the headline workload,
+timed with HIP events on the launch stream, with the L2/MALL flushed between launches.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
+HEADLINE = "decode_mha_bf16"
+SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16"]
+TILING = {
+    "decode_mha_bf16": dict(dec_split=512),
+    "decode_gqa_bf16_bs16": dict(dec_split=512),
+    "decode_gqa_bf16_bs64": dict(dec_split=512),
+    "prefill_varlen_bf16": dict(pf_q_tile=128, pf_kv_split=0),
+    "mixed_bf16": dict(dec_split=512, pf_q_tile=128, pf_kv_split=8192),
+}
+
+
+def algorithmic_work(w):
+    """Bytes the method must move and flops it must do, counting valid data only: every
+    visible K/V row once, q and out once, the block-table entries a sequence needs, its
+    length; flops = 4*D per unmasked (query row, key) pair per query head."""
+    esize = 2 if w.dtype == "bf16" else 4
+    e_kv = 2 * w.num_kv_heads * w.head_dim * esize
+    ctx = w.ctx_lens.astype(np.int64)
+    q = w.q_lens.astype(np.int64)
+    nblk = (ctx + w.block_size - 1) // w.block_size
+    T = int(q.sum())
+    B = int(ctx.sum()) * e_kv + T * w.num_q_heads * w.head_dim * esize * 2 + int(nblk.sum()) * 4 \
+        + 4 * w.num_seqs
+    P = ctx - q
+    pairs = P * q + q * (q + 1) // 2                      # sum over rows i of (P + i + 1)
+    dec = q == 1
+    F_dec = int((pairs[dec]).sum()) * w.num_q_heads * 4 * w.head_dim
+    F_pre = int((pairs[~dec]).sum()) * w.num_q_heads * 4 * w.head_dim
+    B_dec = int(ctx[dec].sum()) * e_kv + int(dec.sum()) * w.num_q_heads * w.head_dim * esize * 2 \
+        + int(nblk[dec].sum()) * 4 + 4 * int(dec.sum())
+    return dict(bytes=B, flops_prefill=F_pre, flops_decode=F_dec, bytes_decode=B_dec,
+                reshape_bytes=2 * 2 * T * w.num_kv_heads * w.head_dim * esize)
+
+
+class Runner:
+    """Everything one workload's step needs, resident on the GPU."""
+
+    def __init__(self, name, seed=None):
+        import torch
+        import synth
+        import paged_variable_length_amd as pa
+        self.torch, self.pa = torch, pa
+        self.name = name
+        self.w = w = synth.make_workload(name, seed)
+        self.vals = synth.make_values(w, device="cuda", nan_sentinels=True)
+        self.tiling = dict(TILING[name], num_workers=256 * 2)
+        self.cu_host = pa.pack_seqlens(w.q_lens)
+        self.ctx_host = w.ctx_lens.astype(np.int32)
+        self.params = pa.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                     **self.tiling)
+        first = pa.build_task_table(self.params, self.cu_host, self.ctx_host)
+        self.balance = (first.balance_snake, first.balance_modulo)
+        self.num_tasks, self.num_combines = len(first.tasks), len(first.combines)
+        self.num_partials = first.num_partials
+        dev = "cuda"
+        self.cu = torch.from_numpy(self.cu_host).to(dev)
+        self.ctx = torch.from_numpy(self.ctx_host).to(dev)
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        cap_t, cap_c = max(self.num_tasks, 1), max(self.num_combines, 1)
+        self.pin_t = [torch.zeros((cap_t, 8), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.pin_c = [torch.zeros((cap_c, 8), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev_t = [torch.zeros((cap_t, 8), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.dev_c = [torch.zeros((cap_c, 8), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.slot_ev = [None, None]
+        nbytes = pa.workspace_bytes(self.num_partials, w.head_dim)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(self.vals["q"])
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+        self.decode_only = bool(np.all(w.q_lens == 1))
+        self.work = algorithmic_work(w)
+        self.step_no = 0
+
+    def step(self, ev_pair=None):
+        """One full step; optionally brackets the attention launch with (start, stop) events."""
+        torch, pa, v = self.torch, self.pa, self.vals
+        k = self.step_no % 2
+        self.step_no += 1
+        if self.slot_ev[k] is not None:
+            self.slot_ev[k].synchronize()      # the slot's previous copy and kernels are done
+        t = pa.build_task_table(self.params, self.cu_host, self.ctx_host, self.pin_t[k].numpy(),
+                                self.pin_c[k].numpy(), with_balance=False)
+        nt, nc = len(t.tasks), len(t.combines)
+        self.dev_t[k][:nt].copy_(self.pin_t[k][:nt], non_blocking=True)
+        if nc:
+            self.dev_c[k][:nc].copy_(self.pin_c[k][:nc], non_blocking=True)
+        pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt, self.cu,
+                             self.ctx)
+        if ev_pair is not None:
+            ev_pair[0].record()
+        if self.decode_only:
+            pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
+                                 self.dev_t[k][:nt], self.dev_c[k][:nc], t.num_partials, self.ws,
+                                 self.out)
+        else:
+            pa.paged_attn_varlen_prefill(v["q"], v["k_pages"], v["v_pages"], self.bt, self.cu,
+                                         self.ctx, self.scale, self.dev_t[k][:nt],
+                                         self.dev_c[k][:nc], t.num_partials, self.ws, self.out)
+        if ev_pair is not None:
+            ev_pair[1].record()
+        ev = torch.cuda.Event()
+        ev.record()
+        self.slot_ev[k] = ev
+
+    def timed_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def launch_times(self, launches, flush):
+        """Average duration of the attention launch (HIP events on the current stream, which the
+        library launches on), with L2/MALL flushed by a 512 MiB write between launches."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for e in evs:
+            flush.fill_(1)
+            self.step(e)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        return float(np.mean(ms)), float(np.min(ms))
+
+    def finite(self):
+        return bool(self.torch.isfinite(self.out).all())
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded seeded sample of the same workload's
+    sequences (cache scatter + attention), timed on this host's cores."""
+    import torch
+    import synth
+    from oracle import attention as oa
+    from oracle import cache as oc
+    w = synth.make_workload(name)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.num_seqs)
+    vals = synth.make_values(w, device="cuda", nan_sentinels=False)
+    esize = 2 if w.dtype == "bf16" else 4
+    e_kv = 2 * w.num_kv_heads * w.head_dim * esize
+    cu = oa.pack_lengths(w.q_lens)
+    done_bytes, done_seqs, spent = 0, 0, 0.0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    for s in order:
+        s = int(s)
+        nblk = oa.blocks_needed(int(w.ctx_lens[s]), w.block_size)
+        ids = torch.from_numpy(w.block_table[s, :nblk].astype(np.int64)).cuda()
+        kp = vals["k_pages"].index_select(0, ids).float().cpu().numpy().astype(np.float64)
+        vp = vals["v_pages"].index_select(0, ids).float().cpu().numpy().astype(np.float64)
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        q = vals["q"][rows].float().cpu().numpy().astype(np.float64)
+        kn = vals["k_new"][rows].float().cpu().numpy().astype(np.float64)
+        vn = vals["v_new"][rows].float().cpu().numpy().astype(np.float64)
+        table = np.arange(nblk)[None, :]
+        ql, ctx = w.q_lens[s:s + 1], w.ctx_lens[s:s + 1]
+        t0 = time.perf_counter()
+        kp2, vp2 = oc.reshape_and_cache(kn, vn, kp, vp, table, ql, ctx)
+        oa.paged_attention_fast(q, kp2, vp2, table, ql, ctx, 1.0 / math.sqrt(w.head_dim))
+        spent += time.perf_counter() - t0
+        done_bytes += int(ctx[0]) * e_kv + int(ql[0]) * w.num_q_heads * w.head_dim * esize * 2 \
+            + nblk * 4 + 4
+        done_seqs += 1
+        if spent >= budget_s:
+            break
+    del vals
+    torch.cuda.empty_cache()
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done_seqs} of {w.num_seqs} sequences of {name} (seeded order), "
+                      f"fp64 NumPy cache scatter + attention, {spent:.1f} s"}
+
+
+def run(name, steps, warmup, with_launch_timing=True, flush=None):
+    r = Runner(name)
+    step_s = r.timed_steps(steps, warmup)
+    res = {"workload": name, "ms_per_step": round(step_s * 1e3, 4), "tasks": r.num_tasks,
+           "combines": r.num_combines, "balance_snake": round(r.balance[0], 4),
+           "balance_modulo": round(r.balance[1], 4), "finite": r.finite(), "work": r.work,
+           "tiling": r.tiling}
+    if with_launch_timing:
+        avg_ms, min_ms = r.launch_times(max(steps, 10), flush)
+        res["attn_launch_ms_avg"] = round(avg_ms, 4)
+        res["attn_launch_ms_min"] = round(min_ms, 4)
+    del r
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
+
+    if args.calibrate_copy:
+        src = torch.ones(2**28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+
+    head = run(args.workload, args.steps, args.warmup, True, flush)
+    print(f"[bench] {args.workload}: {head['ms_per_step']} ms/step, attention launch "
+          f"{head['attn_launch_ms_avg']} ms", file=sys.stderr, flush=True)
+    secondary = {}
+    if not args.only:
+        for name in SECONDARY:
+            if name == args.workload:
+                continue
+            res = run(name, args.steps, args.warmup, True, flush)
+            wk = res["work"]
+            t_launch = res["attn_launch_ms_avg"] * 1e-3
+            res["attn_gbs"] = round(wk["bytes"] / t_launch / 1e9, 1)
+            res["attn_tflops_prefill"] = round(wk["flops_prefill"] / t_launch / 1e12, 2)
+            res["hbm_frac"] = round(res["attn_gbs"] / HBM_PEAK_GBS, 4)
+            res["mfma_frac"] = round(res["attn_tflops_prefill"] / MFMA_BF16_PEAK_TFLOPS, 4)
+            res["roofline_frac"] = round(max(wk["bytes"] / (HBM_PEAK_GBS * 1e9),
+                                             wk["flops_prefill"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                                         / t_launch, 4)
+            secondary[name] = res
+            print(f"[bench] {name}: {res['ms_per_step']} ms/step, launch "
+                  f"{res['attn_launch_ms_avg']} ms, {res['attn_gbs']} GB/s, "
+                  f"{res['attn_tflops_prefill']} TFLOP/s", file=sys.stderr, flush=True)
+
+    wk = head["work"]
+    step_s = head["ms_per_step"] * 1e-3
+    value = wk["bytes"] / step_s / 1e9
+    achieved = wk["bytes"] / (head["attn_launch_ms_avg"] * 1e-3) / 1e9
+    w = head
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload)
+    import synth
+    wl = synth.make_workload(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and shuffled block pool)",
+        "config": {"workload": args.workload, "num_seqs": wl.num_seqs,
+                   "context_lens": "uniform [128, 4096]" if args.workload == HEADLINE else "see synth",
+                   "sum_context": int(wl.ctx_lens.sum()), "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block_size": wl.block_size, **TILING[args.workload]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode launch (decode_kernel + combine_kernel)",
+                     "bytes_per_launch": wk["bytes"],
+                     "launch_ms_avg": head["attn_launch_ms_avg"],
+                     "launch_ms_min": head["attn_launch_ms_min"]},
+        "cpu_baseline": cpu,
+        "headline_detail": {k: head[k] for k in ("tasks", "combines", "balance_snake",
+                                                 "balance_modulo", "finite")},
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

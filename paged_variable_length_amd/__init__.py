@@ -63,26 +63,40 @@ class TaskTable:
     balance_modulo: float
 
 
-def build_task_table(params: PaParams, cu_seqlens_q, context_lens) -> TaskTable:
-    """Host task table (library call); two-call sizing through PA_ERR_CAPACITY."""
+def build_task_table(params: PaParams, cu_seqlens_q, context_lens, tasks_out=None,
+                     combines_out=None, with_balance=True) -> TaskTable:
+    """Host task table (library call).
+
+    Without output buffers the table is sized with a first call (PA_ERR_CAPACITY) and filled
+    by a second. With ``tasks_out`` / ``combines_out`` (int32 [cap, 8] numpy arrays, e.g. views
+    of pinned host memory) it is one call that writes into them; the returned TaskTable then
+    holds views of the filled rows.
+    """
     L = lib()
     cu = _i32(cu_seqlens_q)
     ctx = _i32(context_lens)
     n = ctx.shape[0]
     nt, nc, npart = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    bal = (ctypes.c_double * 2)()
-    rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, None, 0,
-                            ctypes.byref(nt), None, 0, ctypes.byref(nc), ctypes.byref(npart), bal)
-    if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
-        check(rc, "build_task_table")
-    tasks = np.zeros((nt.value, 8), dtype=np.int32)
-    comb = np.zeros((nc.value, 8), dtype=np.int32)
+    bal = (ctypes.c_double * 2)() if with_balance else None
+    if tasks_out is None:
+        rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, None, 0,
+                                ctypes.byref(nt), None, 0, ctypes.byref(nc),
+                                ctypes.byref(npart), None)
+        if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
+            check(rc, "build_task_table")
+        tasks_out = np.zeros((nt.value, 8), dtype=np.int32)
+        combines_out = np.zeros((nc.value, 8), dtype=np.int32)
+    for a in (tasks_out, combines_out):
+        if a.dtype != np.int32 or a.ndim != 2 or a.shape[1] != 8 or not a.flags.c_contiguous:
+            raise ValueError("table buffers must be contiguous int32 [cap, 8]")
     rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n,
-                            tasks.ctypes.data_as(ctypes.POINTER(PaTask)), nt.value,
-                            ctypes.byref(nt), comb.ctypes.data_as(ctypes.POINTER(PaCombine)),
-                            nc.value, ctypes.byref(nc), ctypes.byref(npart), bal)
+                            tasks_out.ctypes.data_as(ctypes.POINTER(PaTask)), tasks_out.shape[0],
+                            ctypes.byref(nt), combines_out.ctypes.data_as(ctypes.POINTER(PaCombine)),
+                            combines_out.shape[0], ctypes.byref(nc), ctypes.byref(npart), bal)
     check(rc, "build_task_table")
-    return TaskTable(tasks, comb, npart.value, bal[0], bal[1])
+    return TaskTable(tasks_out[:nt.value], combines_out[:nc.value], npart.value,
+                     bal[0] if bal is not None else float("nan"),
+                     bal[1] if bal is not None else float("nan"))
 
 
 def workspace_bytes(num_partials: int, head_dim: int) -> int:

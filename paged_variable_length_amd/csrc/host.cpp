@@ -83,6 +83,142 @@ double ratio(const std::vector<int64_t>& v) {
   return mx == 0 ? 1.0 : static_cast<double>(mn) / static_cast<double>(mx);
 }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Unmasked (row, key) pairs of a causal tile split: the rows see key counts e = e0 .. e1
+// (row at position p sees keys 0 .. p, i.e. e = p + 1 keys), and within the split [kv0, kv1)
+// a row with count e contributes clamp(e, kv0, kv1) - kv0 pairs. Summed in closed form:
+// counts in (kv0, kv1) add e - kv0 each (an arithmetic series); counts >= kv1 add kv1 - kv0.
+int64_t tile_pairs(int64_t e0, int64_t e1, int64_t kv0, int64_t kv1) {
+  int64_t total = 0;
+  const int64_t lo = std::max(e0, kv0 + 1), hi = std::min(e1, kv1 - 1);
+  if (lo <= hi) total += (lo + hi) * (hi - lo + 1) / 2 - kv0 * (hi - lo + 1);
+  const int64_t full_lo = std::max(e0, kv1);
+  if (e1 >= full_lo) total += (e1 - full_lo + 1) * (kv1 - kv0);
+  return total;
+}
+
+// Emission order of the decomposition: sequences ascending; decode sequences give kv head,
+// then key split; prefill sequences give query head, then query tile, then key split.
+// `emit(load, task)` and `combine(record)` receive every item in that order, and the partial
+// rows are numbered in the same order.
+template <class EmitF, class CombF>
+void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
+               EmitF&& emit, CombF&& combine, int64_t* num_partials) {
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  int64_t parts = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ql = cu[s + 1] - cu[s];
+    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
+    if (ql == 1) {
+      // decode: key splits of dec_split per kv head, all G query heads in one task
+      const int32_t nsplit = static_cast<int32_t>(ceil_div(ctx[s], p->dec_split));
+      for (int32_t g = 0; g < p->num_kv_heads; ++g) {
+        int64_t first = -1;
+        if (nsplit > 1) {
+          first = parts;
+          parts += static_cast<int64_t>(nsplit) * G;
+          combine(pa_combine{s, 0, 1, g * G, G, static_cast<int32_t>(first), nsplit, 0});
+        }
+        for (int32_t k = 0; k < nsplit; ++k) {
+          const int32_t kv0 = k * p->dec_split;
+          const int32_t kv1 = std::min(ctx[s], kv0 + p->dec_split);
+          const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * G) : -1;
+          emit(int64_t(kv1 - kv0) * G * p->decode_weight,
+               pa_task{PA_TASK_DECODE, s, g, 0, 1, kv0, kv1, part});
+        }
+      }
+    } else {
+      // prefill: causal query tiles per query head, each split along its visible keys
+      for (int32_t h = 0; h < p->num_q_heads; ++h) {
+        for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
+          const int32_t rows = std::min(p->pf_q_tile, ql - r0);
+          const int64_t lim = prefix + r0 + rows;  // keys visible to the tile's last row
+          const int64_t split = p->pf_kv_split > 0 ? p->pf_kv_split : lim;
+          const int32_t nsplit = static_cast<int32_t>(ceil_div(lim, split));
+          int64_t first = -1;
+          if (nsplit > 1) {
+            first = parts;
+            parts += static_cast<int64_t>(nsplit) * rows;
+            combine(pa_combine{s, r0, rows, h, 1, static_cast<int32_t>(first), nsplit, 0});
+          }
+          for (int32_t k = 0; k < nsplit; ++k) {
+            const int64_t kv0 = k * split;
+            const int64_t kv1 = std::min(lim, kv0 + split);
+            const int64_t load = tile_pairs(prefix + r0 + 1, prefix + r0 + rows, kv0, kv1);
+            const int32_t part =
+                nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * rows) : -1;
+            emit(load, pa_task{PA_TASK_PREFILL, s, h, r0, rows, static_cast<int32_t>(kv0),
+                               static_cast<int32_t>(kv1), part});
+          }
+        }
+      }
+    }
+  }
+  *num_partials = parts;
+}
+
+// Task, combine and partial-row counts without emitting anything.
+void count(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
+           int64_t* nt, int64_t* nc, int64_t* np) {
+  const int64_t G = p->num_q_heads / p->num_kv_heads;
+  int64_t t = 0, c = 0, parts = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ql = cu[s + 1] - cu[s];
+    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
+    if (ql == 1) {
+      const int64_t nsplit = ceil_div(ctx[s], p->dec_split);
+      t += nsplit * p->num_kv_heads;
+      if (nsplit > 1) {
+        c += p->num_kv_heads;
+        parts += nsplit * G * p->num_kv_heads;
+      }
+    } else {
+      for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
+        const int64_t rows = std::min(p->pf_q_tile, ql - r0);
+        const int64_t lim = prefix + r0 + rows;
+        const int64_t nsplit = p->pf_kv_split > 0 ? ceil_div(lim, p->pf_kv_split) : 1;
+        t += nsplit * p->num_q_heads;
+        if (nsplit > 1) {
+          c += p->num_q_heads;
+          parts += nsplit * rows * p->num_q_heads;
+        }
+      }
+    }
+  }
+  *nt = t;
+  *nc = c;
+  *np = parts;
+}
+
+// Stable order of `em` by load, descending: LSD radix sort (11-bit digits) on
+// (max_load - load), which keeps equal loads in emission order.
+void sort_by_load_desc(const std::vector<Emitted>& em, std::vector<uint32_t>& order) {
+  const size_t n = em.size();
+  int64_t mx = 0;
+  for (const Emitted& e : em) mx = std::max(mx, e.load);
+  static thread_local std::vector<uint32_t> tmp;
+  order.resize(n);
+  tmp.resize(n);
+  for (size_t i = 0; i < n; ++i) order[i] = static_cast<uint32_t>(i);
+  constexpr int kBits = 11;
+  constexpr uint64_t kMask = (1u << kBits) - 1;
+  std::vector<uint32_t> hist(size_t(1) << kBits);
+  for (int shift = 0; shift < 64 && (static_cast<uint64_t>(mx) >> shift) != 0; shift += kBits) {
+    std::fill(hist.begin(), hist.end(), 0u);
+    for (size_t i = 0; i < n; ++i) ++hist[(static_cast<uint64_t>(mx - em[order[i]].load) >> shift) & kMask];
+    uint32_t run = 0;
+    for (uint32_t& h : hist) {
+      const uint32_t c = h;
+      h = run;
+      run += c;
+    }
+    for (size_t i = 0; i < n; ++i)
+      tmp[hist[(static_cast<uint64_t>(mx - em[order[i]].load) >> shift) & kMask]++] = order[i];
+    order.swap(tmp);
+  }
+}
+
 }  // namespace
 
 // Dynamic Decomposer + load-sorted reorder (XY-Serve page, sections 2.2 and 4.4).
@@ -102,89 +238,50 @@ extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int
       return set_error(PA_ERR_INPUT, "context_lens[%d] = %d is shorter than its %d query rows",
                        s, ctx[s], cu[s + 1] - cu[s]);
   }
-  const int32_t G = p->num_q_heads / p->num_kv_heads;
-  std::vector<Emitted> em;
-  std::vector<pa_combine> comb;
-  int64_t parts = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t ql = cu[s + 1] - cu[s];
-    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
-    if (ql == 1) {
-      // decode: key splits of dec_split per kv head, all G query heads in one task
-      const int32_t nsplit =
-          static_cast<int32_t>((int64_t(ctx[s]) + p->dec_split - 1) / p->dec_split);
-      for (int32_t g = 0; g < p->num_kv_heads; ++g) {
-        int64_t first = -1;
-        if (nsplit > 1) {
-          first = parts;
-          parts += static_cast<int64_t>(nsplit) * G;
-          comb.push_back(pa_combine{s, 0, 1, g * G, G, static_cast<int32_t>(first), nsplit, 0});
-        }
-        for (int32_t k = 0; k < nsplit; ++k) {
-          const int32_t kv0 = k * p->dec_split;
-          const int32_t kv1 = std::min(ctx[s], kv0 + p->dec_split);
-          const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * G) : -1;
-          const int64_t load = int64_t(kv1 - kv0) * G * p->decode_weight;
-          em.push_back(Emitted{load, pa_task{PA_TASK_DECODE, s, g, 0, 1, kv0, kv1, part}});
-        }
-      }
-    } else {
-      // prefill: causal query tiles per query head, each split along its visible keys
-      for (int32_t h = 0; h < p->num_q_heads; ++h) {
-        for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
-          const int32_t rows = std::min(p->pf_q_tile, ql - r0);
-          const int64_t lim = prefix + r0 + rows;  // keys visible to the tile's last row
-          const int64_t split = p->pf_kv_split > 0 ? p->pf_kv_split : lim;
-          const int32_t nsplit = static_cast<int32_t>((lim + split - 1) / split);
-          int64_t first = -1;
-          if (nsplit > 1) {
-            first = parts;
-            parts += static_cast<int64_t>(nsplit) * rows;
-            comb.push_back(pa_combine{s, r0, rows, h, 1, static_cast<int32_t>(first), nsplit, 0});
-          }
-          for (int32_t k = 0; k < nsplit; ++k) {
-            const int64_t kv0 = k * split;
-            const int64_t kv1 = std::min(lim, kv0 + split);
-            int64_t load = 0;
-            for (int32_t i = r0; i < r0 + rows; ++i)
-              load += std::max<int64_t>(0, std::min(kv1, prefix + i + 1) - kv0);
-            const int32_t part =
-                nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * rows) : -1;
-            em.push_back(Emitted{load, pa_task{PA_TASK_PREFILL, s, h, r0, rows,
-                                               static_cast<int32_t>(kv0),
-                                               static_cast<int32_t>(kv1), part}});
-          }
-        }
-      }
-    }
-    if (parts > INT32_MAX || em.size() > size_t(INT32_MAX))
-      return set_error(PA_ERR_SHAPE, "task table exceeds int32 indexing");
+  int64_t nt = 0, nc = 0, np = 0;
+  count(p, cu, ctx, num_seqs, &nt, &nc, &np);
+  if (nt > INT32_MAX || nc > INT32_MAX || np > INT32_MAX)
+    return set_error(PA_ERR_SHAPE, "task table exceeds int32 indexing");
+  *num_tasks = static_cast<int32_t>(nt);
+  *num_combines = static_cast<int32_t>(nc);
+  *num_partials = static_cast<int32_t>(np);
+  if (nt > tasks_cap || nc > combines_cap) {
+    if (balance) balance[0] = balance[1] = 0.0;
+    return set_error(PA_ERR_CAPACITY, "need %lld tasks (cap %d) and %lld combines (cap %d)",
+                     static_cast<long long>(nt), tasks_cap, static_cast<long long>(nc),
+                     combines_cap);
   }
-  // stable sort by load, descending: ties keep emission order
-  std::stable_sort(em.begin(), em.end(),
-                   [](const Emitted& a, const Emitted& b) { return a.load > b.load; });
-  *num_tasks = static_cast<int32_t>(em.size());
-  *num_combines = static_cast<int32_t>(comb.size());
-  *num_partials = static_cast<int32_t>(parts);
+  if (nt > 0 && !tasks) return set_error(PA_ERR_NULL, "build_task_table: tasks is NULL");
+  if (nc > 0 && !combines) return set_error(PA_ERR_NULL, "build_task_table: combines is NULL");
+
+  static thread_local std::vector<Emitted> em;
+  static thread_local std::vector<uint32_t> order;
+  em.clear();
+  em.reserve(static_cast<size_t>(nt));
+  int64_t nci = 0, parts = 0;
+  decompose(
+      p, cu, ctx, num_seqs, [&](int64_t load, const pa_task& t) { em.push_back(Emitted{load, t}); },
+      [&](const pa_combine& c) {
+        if (nci < nc) combines[nci] = c;
+        ++nci;
+      },
+      &parts);
+  if (static_cast<int64_t>(em.size()) != nt || nci != nc || parts != np)
+    return set_error(PA_ERR_SHAPE, "build_task_table: internal count mismatch");
+  sort_by_load_desc(em, order);
+  for (size_t i = 0; i < em.size(); ++i) tasks[i] = em[order[i]].task;
   if (balance) {
     const int32_t W = p->num_workers;
     std::vector<int64_t> snake(W, 0), modulo(W, 0);
     for (size_t i = 0; i < em.size(); ++i) {
+      const int64_t ld = em[order[i]].load;
       const size_t rnd = i / W, pos = i % W;
-      snake[rnd % 2 == 0 ? pos : W - 1 - pos] += em[i].load;
-      modulo[i % W] += em[i].load;
+      snake[rnd % 2 == 0 ? pos : W - 1 - pos] += ld;
+      modulo[i % W] += ld;
     }
     balance[0] = ratio(snake);
     balance[1] = ratio(modulo);
   }
-  if (static_cast<int64_t>(em.size()) > tasks_cap || static_cast<int64_t>(comb.size()) > combines_cap)
-    return set_error(PA_ERR_CAPACITY, "need %zu tasks (cap %d) and %zu combines (cap %d)",
-                     em.size(), tasks_cap, comb.size(), combines_cap);
-  if (!em.empty() && !tasks) return set_error(PA_ERR_NULL, "build_task_table: tasks is NULL");
-  if (!comb.empty() && !combines)
-    return set_error(PA_ERR_NULL, "build_task_table: combines is NULL");
-  for (size_t i = 0; i < em.size(); ++i) tasks[i] = em[i].task;
-  if (!comb.empty()) std::memcpy(combines, comb.data(), comb.size() * sizeof(pa_combine));
   return pa::clear_error();
 }
 
