@@ -106,11 +106,9 @@ class Runner:
         self.work = algorithmic_work(w)
         self.step_no = 0
 
-    def step(self, ev_pair=None):
-        """One full step; optionally brackets the attention launch with (start, stop) events."""
-        torch, pa, v = self.torch, self.pa, self.vals
-        k = self.step_no % 2
-        self.step_no += 1
+    def build_table(self, k):
+        """Host table for slot k into pinned memory, then an async copy to the device slot."""
+        pa = self.pa
         if self.slot_ev[k] is not None:
             self.slot_ev[k].synchronize()      # the slot's previous copy and kernels are done
         t = pa.build_task_table(self.params, self.cu_host, self.ctx_host, self.pin_t[k].numpy(),
@@ -119,21 +117,32 @@ class Runner:
         self.dev_t[k][:nt].copy_(self.pin_t[k][:nt], non_blocking=True)
         if nc:
             self.dev_c[k][:nc].copy_(self.pin_c[k][:nc], non_blocking=True)
+        return nt, nc, t.num_partials
+
+    def launch(self, k, nt, nc, nparts, ev_pair=None):
+        """Cache write, then the attention launch (bracketed by ev_pair if given)."""
+        pa, v = self.pa, self.vals
         pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt, self.cu,
                              self.ctx)
         if ev_pair is not None:
             ev_pair[0].record()
         if self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
-                                 self.dev_t[k][:nt], self.dev_c[k][:nc], t.num_partials, self.ws,
-                                 self.out)
+                                 self.dev_t[k][:nt], self.dev_c[k][:nc], nparts, self.ws, self.out)
         else:
             pa.paged_attn_varlen_prefill(v["q"], v["k_pages"], v["v_pages"], self.bt, self.cu,
                                          self.ctx, self.scale, self.dev_t[k][:nt],
-                                         self.dev_c[k][:nc], t.num_partials, self.ws, self.out)
+                                         self.dev_c[k][:nc], nparts, self.ws, self.out)
         if ev_pair is not None:
             ev_pair[1].record()
-        ev = torch.cuda.Event()
+
+    def step(self):
+        """One full step: host table (slot k), its copy, cache write, attention."""
+        k = self.step_no % 2
+        self.step_no += 1
+        nt, nc, nparts = self.build_table(k)
+        self.launch(k, nt, nc, nparts)
+        ev = self.torch.cuda.Event()
         ev.record()
         self.slot_ev[k] = ev
 
@@ -149,14 +158,19 @@ class Runner:
         return (time.perf_counter() - t0) / steps
 
     def launch_times(self, launches, flush):
-        """Average duration of the attention launch (HIP events on the current stream, which the
-        library launches on), with L2/MALL flushed by a 512 MiB write between launches."""
+        """Average duration of the attention launch, from HIP events recorded on the current
+        stream (the stream the library launches on). The table is built once; each iteration
+        flushes L2/MALL with a 512 MiB write, rewrites the cache, and brackets the attention
+        launch. Nothing synchronises the host inside the loop, so the queue stays full and the
+        events time the GPU work, not host launch latency."""
         torch = self.torch
+        torch.cuda.synchronize()
+        nt, nc, nparts = self.build_table(0)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(launches)]
         for e in evs:
             flush.fill_(1)
-            self.step(e)
+            self.launch(0, nt, nc, nparts, e)
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in evs]
         return float(np.mean(ms)), float(np.min(ms))
