@@ -381,26 +381,38 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
 //   S^T C-layout:  reg r of key block kb = S[row i32][key 32*kb + 8*(r/4) + 4*g2 + r%4].
 //   PV (32x32x16): A = V^T [32 d-rows x 16 keys], B = P^T [16 keys x 32 rows];
 //                  k-step kk, slot (g2, e) <-> key 16*kk + 8*(e/4) + 4*g2 + e%4,
-//                  d-row i32 of block n <-> d = DV*i32 + n.
-//   O^T C-layout:  acc[n] reg r = O[row i32][d = DV*(8*(r/4) + 4*g2 + r%4) + n].
+//                  d-row i of block n <-> d = 32*n + i.
+//   O^T C-layout:  acc[n] reg r = O[row i32][d = 32*n + 8*(r/4) + 4*g2 + r%4].
+// K/V tiles reach LDS by direct global->LDS loads (16 bytes per lane, 1 KiB per wave
+// instruction). Rows are stored unpadded with the 16-byte chunks of key row k permuted by
+// XOR with swz(k), so the K reads (eight consecutive keys, one chunk) and the transposed V
+// reads (four keys, two neighbouring chunks) spread over distinct banks.
+// V^T operands come from ds_read_b64_tr_b16: within each 16-lane group, lane j = 4r + c
+// returns element c of the 8-byte segments addressed by lanes r, 4+r, 8+r, 12+r. With lane k
+// of the group addressing key kbase + k/4, d = d0 + 4*(k%4), lane j receives the four keys
+// kbase .. kbase+3 at d = d0 + j -- a column of V, as the MFMA operand needs.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
-  static constexpr int kTile = 64;             // keys per LDS tile
-  static constexpr int kPitch = D + 8;         // LDS row pitch in bf16 (16-byte pad)
-  static constexpr int kChunks = D / 8;        // 16-byte chunks per key row
-  static constexpr int kRowsPerPass = kThreads / kChunks;
-  static constexpr int kPasses = kTile / kRowsPerPass;
-  static constexpr int kTileElems = kTile * kPitch;
-  static constexpr size_t kSmemBytes = 4 * kTileElems * sizeof(uint16_t);  // K, V x 2 buffers
+  static constexpr int kTile = 64;                                  // keys per LDS tile
+  static constexpr int kRowBytes = D * 2;                           // one bf16 key row
+  static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kKeysPerLoad = 1024 / kRowBytes;             // keys per wave load
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;       // per tensor per tile
+  static constexpr size_t kSmemBytes = 4 * static_cast<size_t>(kTileBytes);  // K,V x 2 bufs
 };
 
+__device__ __forceinline__ int lds_swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 template <int D>
-__device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem) {
+__device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   typedef PrefillCfg<D> C;
-  constexpr int KS = D / 16;
+  constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int NB = D / 32;   // 32-row d blocks of O^T
-  constexpr int DV = D / 32;   // d values per lane per key in the V^T operand
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i32 = lane & 31, g2 = lane >> 5;
   const int s = t.seq, h = t.head;
@@ -412,7 +424,7 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
   const int bs = a.block_size;
   const int r0 = t.q_row0, rows = t.q_rows;
   const int kv0 = t.kv0, kv1 = t.kv1;
-  const int qi = r0 + 32 * wave + i32;            // this lane's query row (sequence-relative)
+  const int qi = r0 + 32 * wave + i32;              // this lane's query row (sequence-relative)
   const bool row_ok = qi < r0 + rows;
   const bool wave_active = 32 * wave < rows;
   const int wave_pos_lo = prefix + r0 + 32 * wave;  // position of the wave's first row
@@ -435,34 +447,27 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pages) + kvh * head_stride;
   const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_blocks;
-  uint16_t* sk = smem;                      // [2][kTile][kPitch]
-  uint16_t* sv = smem + 2 * C::kTileElems;  // [2][kTile][kPitch]
+  char* sk = smem;                          // [2][kTileBytes]
+  char* sv = smem + 2 * C::kTileBytes;      // [2][kTileBytes]
 
-  const int chunk = threadIdx.x % C::kChunks;
-  const int krow0 = threadIdx.x / C::kChunks;
-  u32x4 kst[C::kPasses], vst[C::kPasses];
-  auto load_tile = [&](int ts) {
+  // Each wave moves kLoadsPerWave 1 KiB pieces of the K tile and of the V tile. Keys past kv1
+  // are read from key kv1-1 instead (valid memory, finite values); they are masked below.
+  auto issue_tile = [&](int ts, int buf) {
 #pragma unroll
-    for (int j = 0; j < C::kPasses; ++j) {
-      const int key = ts + krow0 + j * C::kRowsPerPass;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < kv1) {
-        const int blk = bt[key >> a.bs_shift];
-        const size_t o = static_cast<size_t>(blk) * block_stride +
-                         static_cast<size_t>(key & (bs - 1)) * D + chunk * 8;
-        kv = *reinterpret_cast<const u32x4*>(kbase + o);
-        vv = *reinterpret_cast<const u32x4*>(vbase + o);
-      }
-      kst[j] = kv;
-      vst[j] = vv;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::kPasses; ++j) {
-      const int r = krow0 + j * C::kRowsPerPass;
-      *reinterpret_cast<u32x4*>(sk + buf * C::kTileElems + r * C::kPitch + chunk * 8) = kst[j];
-      *reinterpret_cast<u32x4*>(sv + buf * C::kTileElems + r * C::kPitch + chunk * 8) = vst[j];
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int piece = wave * C::kLoadsPerWave + i;
+      const int key = piece * C::kKeysPerLoad + lane / C::kChunks;
+      const int chunk = (lane % C::kChunks) ^ lds_swz(key);
+      const int kabs = min(ts + key, kv1 - 1);
+      const int blk = bt[kabs >> a.bs_shift];
+      const size_t o = static_cast<size_t>(blk) * block_stride +
+                       static_cast<size_t>(kabs & (bs - 1)) * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds(
+          kbase + o, (__attribute__((address_space(3))) void*)(sk + buf * C::kTileBytes + piece * 1024),
+          16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vbase + o, (__attribute__((address_space(3))) void*)(sv + buf * C::kTileBytes + piece * 1024),
+          16, 0, 0);
     }
   };
 
@@ -473,27 +478,35 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
+  // V^T operand addressing (see the header comment): group gq = lane / 16, j = lane % 16
+  const int gq = lane >> 4, jq = lane & 15;
+  const int v_key_off = 4 * g2 + (jq >> 2);                 // + 16*kk (+ 8 for the 2nd read)
+  const int v_d = 16 * (gq & 1) + 4 * (jq & 3);             // + 32*n
+  const int v_byte_in_chunk = 8 * (jq & 1);
+
   const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
-  load_tile(kv0);
-  store_tile(0);
+  issue_tile(kv0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int ts = kv0 + it * C::kTile;
     const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(ts + C::kTile);
+    if (it + 1 < ntiles) issue_tile(ts + C::kTile, buf ^ 1);
     // skip tiles whose every key lies after every row of this wave
     if (wave_active && ts <= wave_pos_lo + 31) {
-      const uint16_t* kt = sk + buf * C::kTileElems;
-      const uint16_t* vt = sv + buf * C::kTileElems;
+      const char* kt = sk + buf * C::kTileBytes;
+      const char* vt = sv + buf * C::kTileBytes;
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+        const int key = kb * 32 + i32;
+        const char* krow = kt + key * C::kRowBytes;
+        const int sw = lds_swz(key);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kw =
-              *reinterpret_cast<const u32x4*>(kt + (kb * 32 + i32) * C::kPitch + 16 * ks + 8 * g2);
+          const u32x4 kw = *reinterpret_cast<const u32x4*>(krow + (((2 * ks + g2) ^ sw) << 4));
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qf[ks], sc[kb], 0, 0, 0);
         }
       }
@@ -512,10 +525,19 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx * c);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2(m - muse);
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
+      // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
+      // (weights stay <= 2^8); numerator and denominator share the same reference, so the
+      // result is unchanged.
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+        m = mnew;
+      }
+      const float muse = m == -INFINITY ? 0.f : m;
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -524,10 +546,7 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
           sc[kb][r] = fast_exp2(fmaf(sc[kb][r], c, -muse));
           psum += sc[kb][r];
         }
-      l = l * alpha + psum;
-      m = mnew;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+      l += psum;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int kb = kk >> 1, rb = 8 * (kk & 1);
@@ -536,39 +555,25 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
                     pack_bf16x2(sc[kb][rb + 4], sc[kb][rb + 5]),
                     pack_bf16x2(sc[kb][rb + 6], sc[kb][rb + 7])};
         const bf16x8 pf = as_bf16x8(pw);
-        if constexpr (D == 128) {
-          u32x2 vr[8];
+        const int key1 = 16 * kk + v_key_off;
+        const int key2 = key1 + 8;
+        const char* vrow1 = vt + key1 * C::kRowBytes + v_byte_in_chunk;
+        const char* vrow2 = vt + key2 * C::kRowBytes + v_byte_in_chunk;
+        const int sw1 = lds_swz(key1), sw2 = lds_swz(key2);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = 16 * kk + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            vr[e] = *reinterpret_cast<const u32x2*>(vt + key * C::kPitch + DV * i32);
-          }
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            u32x4 vw;
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-              vw[qd] = pair_half(vr[2 * qd][n >> 1], vr[2 * qd + 1][n >> 1], n & 1);
-            acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
-          }
-        } else {
-          uint32_t vr[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = 16 * kk + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            vr[e] = *reinterpret_cast<const uint32_t*>(vt + key * C::kPitch + DV * i32);
-          }
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            u32x4 vw;
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) vw[qd] = pair_half(vr[2 * qd], vr[2 * qd + 1], n & 1);
-            acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
-          }
+        for (int n = 0; n < NB; ++n) {
+          const int chunk = (32 * n + v_d) >> 3;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vrow1 + ((chunk ^ sw1) << 4)));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vrow2 + ((chunk ^ sw2) << 4)));
+          const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
         }
       }
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -579,33 +584,23 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, uint16_t* smem
     __bf16* orow = static_cast<__bf16*>(a.out) +
                    (static_cast<size_t>(cu0 + qi) * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      // regs 4*rb .. 4*rb+3 of every block n hold DV*4 consecutive d values
-      const int d0 = DV * (8 * rb + 4 * g2);
-      uint32_t w[2 * DV];
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int n = 0; n < NB; n += 2)
-          w[(rr * NB + n) / 2] = pack_bf16x2(acc[n][4 * rb + rr] * inv, acc[n + 1][4 * rb + rr] * inv);
-      if constexpr (D == 128) {
-        *reinterpret_cast<u32x4*>(orow + d0) = u32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4*>(orow + d0 + 8) = u32x4{w[4], w[5], w[6], w[7]};
-      } else {
-        *reinterpret_cast<u32x4*>(orow + d0) = u32x4{w[0], w[1], w[2], w[3]};
+      for (int rb = 0; rb < 4; ++rb) {
+        const int d0 = 32 * n + 8 * rb + 4 * g2;
+        *reinterpret_cast<u32x2*>(orow + d0) =
+            u32x2{pack_bf16x2(acc[n][4 * rb] * inv, acc[n][4 * rb + 1] * inv),
+                  pack_bf16x2(acc[n][4 * rb + 2] * inv, acc[n][4 * rb + 3] * inv)};
       }
-    }
   } else {
     const size_t row = static_cast<size_t>(t.partial) + (qi - r0);
     float* prow = a.ws_acc + row * D;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int d0 = DV * (8 * rb + 4 * g2);
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int n = 0; n < NB; ++n) prow[d0 + rr * NB + n] = acc[n][4 * rb + rr];
-    }
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<f32x4*>(prow + 32 * n + 8 * rb + 4 * g2) =
+            f32x4{acc[n][4 * rb], acc[n][4 * rb + 1], acc[n][4 * rb + 2], acc[n][4 * rb + 3]};
     if (g2 == 0) {
       a.ws_ml[2 * row] = m;
       a.ws_ml[2 * row + 1] = l;
@@ -636,15 +631,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void meta_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
-  __shared__ __attribute__((aligned(16))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
+  __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_DECODE)
     decode_task_bf16<D>(a, t, reinterpret_cast<float*>(smem));
   else
-    prefill_task<D>(a, t, reinterpret_cast<uint16_t*>(smem));
+    prefill_task<D>(a, t, smem);
 }
 
 // One workgroup per combine record; each wave merges one (row, head) at a time.
