@@ -10,7 +10,7 @@ Notation follows the pages:
   * attention is GEMM -> softmax -> GEMM over the sequence's own keys (XY-Serve page, section 2.2,
     "Meta-Attention"), causal (cann-recipes-infer page, section 3.3, is_causal=True).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * context_lens[s] counts the keys visible after this step's cache writes, so the cached prefix
     is P_s = context_lens[s] - q_len_s;
   * causal alignment is bottom-right: query row i of a chunk sits at absolute position P_s + i

@@ -5,7 +5,7 @@ XY-Serve page, section 2.2 ("Token çº§è°ƒåº¦ä¸ä»»åŠ¡åˆ†è§£", "ä»»åŠ¡é‡æ’æœºåˆ
 shape and a compute load, sort the tasks by load from large to small, and report the balance
 ratio min/max of per-core load sums when the sorted tasks are dealt to the cores.
 
-Readings taken where the pages leave the step open (each listed in the design doc):
+Readings taken where the pages leave the step open:
   * decode sequences (one query row) are split along the keys into pieces of ``dec_split``; one
     task covers all query heads of one kv head (grouped-query heads share the KV pages);
   * prefill rows are tiled by ``pf_q_tile`` per query head, and each tile's visible key range

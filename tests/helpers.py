@@ -6,7 +6,9 @@ import numpy as np
 # Attention outputs in bf16 (bf16 inputs, fp32 accumulation) versus the fp64 oracle.
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
-# fp32 inputs: a reading (only the bf16 bounds are stated); derived in the design doc.
+# fp32 inputs (a reading; only the bf16 bounds are stated): fp32 accumulation over <= 64 keys and
+# 128-term dots plus a ~1 ulp exp2 gives O(1e-6) errors on O(1) outputs, so 1e-4 / 1e-5 leaves
+# two orders of margin while a dropped key (weight >= 1/ctx) still fails.
 FP32_MAX_ABS = 1e-4
 FP32_MEAN_ABS = 1e-5
 
