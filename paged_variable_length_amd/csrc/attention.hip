@@ -24,6 +24,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -384,13 +385,15 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
 //                  d-row i of block n <-> d = 32*n + i.
 //   O^T C-layout:  acc[n] reg r = O[row i32][d = 32*n + 8*(r/4) + 4*g2 + r%4].
 // K/V tiles reach LDS by direct global->LDS loads (16 bytes per lane, 1 KiB per wave
-// instruction). Rows are stored unpadded with the 16-byte chunks of key row k permuted by
-// XOR with swz(k), so the K reads (eight consecutive keys, one chunk) and the transposed V
-// reads (four keys, two neighbouring chunks) spread over distinct banks.
+// instruction) into two stages of [K tile | V tile]. Rows are stored unpadded with the 16-byte
+// chunks of key row k permuted by XOR with lds_swz(k), so the K reads and the transposed V
+// reads spread over the banks.
 // V^T operands come from ds_read_b64_tr_b16: within each 16-lane group, lane j = 4r + c
 // returns element c of the 8-byte segments addressed by lanes r, 4+r, 8+r, 12+r. With lane k
 // of the group addressing key kbase + k/4, d = d0 + 4*(k%4), lane j receives the four keys
 // kbase .. kbase+3 at d = d0 + j -- a column of V, as the MFMA operand needs.
+// Every lane-dependent LDS address is computed once per task; stage, key block and k-step
+// enter as instruction offsets, so the tile loop does no address arithmetic for LDS.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
@@ -398,36 +401,88 @@ struct PrefillCfg {
   static constexpr int kRowBytes = D * 2;                           // one bf16 key row
   static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
   static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;                // K tile then V tile
   static constexpr int kKeysPerLoad = 1024 / kRowBytes;             // keys per wave load
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;       // per tensor per tile
-  static constexpr size_t kSmemBytes = 4 * static_cast<size_t>(kTileBytes);  // K,V x 2 bufs
+  static constexpr size_t kSmemBytes = 2 * static_cast<size_t>(kStageBytes);
 };
 
-__device__ __forceinline__ int lds_swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+// XOR pattern of the 16-byte chunks of key row `key` (a permutation of the row's chunks).
+// With 16 chunks per row (D = 128), chunk bits 2-3 follow key bits 0-1 and chunk bits 0-1
+// follow key bits 2-3: sixteen consecutive keys reading one chunk hit sixteen distinct
+// chunk positions, and the transposed reads (four keys x four neighbouring chunks) hit
+// sixteen distinct positions too. Measured on gfx950 with eight waves per CU, this halves the
+// LDS time of both read patterns against a 3-bit pattern and matches an unswizzled
+// contiguous read. With 8 chunks per row (D = 64) a 3-bit pattern is used. The pattern
+// depends on key & 15 only, so shifting a key by a multiple of 16 keeps its pattern.
+template <int D>
+__device__ __forceinline__ int lds_swz(int key) {
+  if constexpr (D == 128)
+    return ((key & 3) << 2) | ((key >> 2) & 3);
+  else
+    return ((key & 3) << 1) | ((key >> 2) & 1);
+}
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// N (4 or 8) LDS reads of one kind at lane addresses a[i] plus the byte offset OFF, issued
+// together and completed before returning. One asm block: the compiler cannot tell that these
+// reads never touch the stage the direct loads are filling and would otherwise wait for those
+// loads first. The block ends with lgkmcnt(0), so nothing it issued is outstanding afterwards.
+#define PA_LDS_READ8(OP, T)                                                                   \
+  template <int OFF>                                                                          \
+  __device__ __forceinline__ void OP##_x8(const uint32_t (&a)[8], T (&r)[8]) {                \
+    asm volatile(#OP " %0, %8 offset:%16\n\t" #OP " %1, %9 offset:%16\n\t"                   \
+                 #OP " %2, %10 offset:%16\n\t" #OP " %3, %11 offset:%16\n\t"                  \
+                 #OP " %4, %12 offset:%16\n\t" #OP " %5, %13 offset:%16\n\t"                  \
+                 #OP " %6, %14 offset:%16\n\t" #OP " %7, %15 offset:%16\n\t"                  \
+                 "s_waitcnt lgkmcnt(0)"                                                       \
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]),           \
+                   "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])                                      \
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),          \
+                   "v"(a[6]), "v"(a[7]), "n"(OFF)                                             \
+                 : "memory");                                                                 \
+  }                                                                                           \
+  template <int OFF>                                                                          \
+  __device__ __forceinline__ void OP##_x4(const uint32_t (&a)[4], T (&r)[4]) {                \
+    asm volatile(#OP " %0, %4 offset:%8\n\t" #OP " %1, %5 offset:%8\n\t"                     \
+                 #OP " %2, %6 offset:%8\n\t" #OP " %3, %7 offset:%8\n\t"                      \
+                 "s_waitcnt lgkmcnt(0)"                                                       \
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])                         \
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(OFF)                       \
+                 : "memory");                                                                 \
+  }
+PA_LDS_READ8(ds_read_b128, u32x4)
+PA_LDS_READ8(ds_read_b64_tr_b16, u32x2)
+#undef PA_LDS_READ8
+
+typedef __attribute__((address_space(4))) const int32_t cint32;
 
 template <int D>
 __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   typedef PrefillCfg<D> C;
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int NB = D / 32;   // 32-row d blocks of O^T
+  constexpr int P = C::kLoadsPerWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i32 = lane & 31, g2 = lane >> 5;
-  const int s = t.seq, h = t.head;
-  const int cu0 = a.cu_seqlens[s];
-  const int ql = a.cu_seqlens[s + 1] - cu0;
-  const int prefix = a.context_lens[s] - ql;
+  // task fields and per-sequence scalars are wave-uniform; readfirstlane lets the compiler
+  // keep everything derived from them (block ids, tile bounds, branches) in scalar registers
+  const int s = __builtin_amdgcn_readfirstlane(t.seq);
+  const int h = __builtin_amdgcn_readfirstlane(t.head);
+  const int cu0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s]);
+  const int ql = __builtin_amdgcn_readfirstlane(a.cu_seqlens[s + 1]) - cu0;
+  const int prefix = __builtin_amdgcn_readfirstlane(a.context_lens[s]) - ql;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / G;
   const int bs = a.block_size;
-  const int r0 = t.q_row0, rows = t.q_rows;
-  const int kv0 = t.kv0, kv1 = t.kv1;
+  const int r0 = __builtin_amdgcn_readfirstlane(t.q_row0);
+  const int rows = __builtin_amdgcn_readfirstlane(t.q_rows);
+  const int kv0 = __builtin_amdgcn_readfirstlane(t.kv0);
+  const int kv1 = __builtin_amdgcn_readfirstlane(t.kv1);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int qi = r0 + 32 * wave + i32;              // this lane's query row (sequence-relative)
   const bool row_ok = qi < r0 + rows;
-  const bool wave_active = 32 * wave < rows;
-  const int wave_pos_lo = prefix + r0 + 32 * wave;  // position of the wave's first row
+  const bool wave_active = 32 * wave_u < rows;
+  const int wave_pos_lo = prefix + r0 + 32 * wave_u;  // position of the wave's first row
   const float c = a.scale_log2;
 
   bf16x8 qf[KS];
@@ -446,28 +501,67 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pages) + kvh * head_stride;
-  const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_blocks;
-  char* sk = smem;                          // [2][kTileBytes]
-  char* sv = smem + 2 * C::kTileBytes;      // [2][kTileBytes]
+  cint32* bt = (cint32*)(a.block_table + static_cast<size_t>(s) * a.max_blocks);
 
-  // Each wave moves kLoadsPerWave 1 KiB pieces of the K tile and of the V tile. Keys past kv1
-  // are read from key kv1-1 instead (valid memory, finite values); they are masked below.
-  auto issue_tile = [&](int ts, int buf) {
+  // ---- lane-constant LDS addresses (stage 0; stage, key block and k-step are offsets)
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  uint32_t ka[KS];                          // K row i32, chunk 2*ks + g2
 #pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const int piece = wave * C::kLoadsPerWave + i;
-      const int key = piece * C::kKeysPerLoad + lane / C::kChunks;
-      const int chunk = (lane % C::kChunks) ^ lds_swz(key);
-      const int kabs = min(ts + key, kv1 - 1);
-      const int blk = bt[kabs >> a.bs_shift];
-      const size_t o = static_cast<size_t>(blk) * block_stride +
-                       static_cast<size_t>(kabs & (bs - 1)) * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds(
-          kbase + o, (__attribute__((address_space(3))) void*)(sk + buf * C::kTileBytes + piece * 1024),
-          16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          vbase + o, (__attribute__((address_space(3))) void*)(sv + buf * C::kTileBytes + piece * 1024),
-          16, 0, 0);
+  for (int ks = 0; ks < KS; ++ks)
+    ka[ks] = lds0 + i32 * C::kRowBytes + (((2 * ks + g2) ^ lds_swz<D>(i32)) << 4);
+  const int gq = lane >> 4, jq = lane & 15;
+  const int v_key = 4 * g2 + (jq >> 2);     // key of this lane's segment (+ 16*kk, + 8)
+  const int v_d = 16 * (gq & 1) + 4 * (jq & 3);
+  uint32_t va[2 * NB];                      // [2n + half]: d block n, keys +8*half
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int key = v_key + 8 * hf;
+      va[2 * n + hf] = lds0 + C::kTileBytes + key * C::kRowBytes +
+                       ((((32 * n + v_d) >> 3) ^ lds_swz<D>(key)) << 4) + 8 * (jq & 1);
+    }
+  // ---- direct-load addressing. A wave's piece i covers kKeysPerLoad keys starting at a
+  // multiple of kKeysPerLoad, all in one block, so it needs one wave-uniform block id (a
+  // scalar load through the constant address space). Within a block the key's slot is
+  // (ts & (bs-1)) + (key_in_tile & (bs-1)) for 64-aligned tiles, so the lane part is constant.
+  uint32_t dma_off[P];                      // lane byte offset inside the (block, kv head) page
+  int dma_key[P];                           // lane's key within the tile
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int key = (wave_u * P + i) * C::kKeysPerLoad + lane / C::kChunks;
+    const int chunk = (lane % C::kChunks) ^ lds_swz<D>(key);
+    dma_key[i] = key;
+    dma_off[i] = (key & (bs - 1)) * C::kRowBytes + chunk * 16;
+  }
+  auto block_ids = [&](int ts, int (&ids)[P]) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int kp = min(ts + (wave_u * P + i) * C::kKeysPerLoad, kv1 - 1);
+      ids[i] = bt[kp >> a.bs_shift];
+    }
+  };
+  // Keys past kv1 (last tile only) are read from key kv1-1 instead (valid memory, finite
+  // values); they are masked in the scores.
+  auto issue_tile = [&](int ts, const int (&ids)[P], int stage) {
+    const bool full = ts + C::kTile <= kv1;
+    const size_t tile_slot = static_cast<size_t>(ts & (bs - 1)) * C::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const size_t page = static_cast<size_t>(ids[i]) * block_stride * 2;
+      uint32_t off = dma_off[i];
+      size_t base = page + tile_slot;
+      if (!full) {
+        const int kabs = min(ts + dma_key[i], kv1 - 1);
+        base = page;
+        off = (kabs & (bs - 1)) * C::kRowBytes + (dma_off[i] & (C::kRowBytes - 1));
+      }
+      char* dst = smem + stage * C::kStageBytes + (wave_u * P + i) * 1024;
+      const char* ksrc = reinterpret_cast<const char*>(kbase) + base + off;
+      const char* vsrc = reinterpret_cast<const char*>(vbase) + base + off;
+      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(dst + C::kTileBytes),
+                                       16, 0, 0);
     }
   };
 
@@ -478,101 +572,139 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // V^T operand addressing (see the header comment): group gq = lane / 16, j = lane % 16
-  const int gq = lane >> 4, jq = lane & 15;
-  const int v_key_off = 4 * g2 + (jq >> 2);                 // + 16*kk (+ 8 for the 2nd read)
-  const int v_d = 16 * (gq & 1) + 4 * (jq & 3);             // + 32*n
-  const int v_byte_in_chunk = 8 * (jq & 1);
-
-  const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
-  issue_tile(kv0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int ts = kv0 + it * C::kTile;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) issue_tile(ts + C::kTile, buf ^ 1);
-    // skip tiles whose every key lies after every row of this wave
-    if (wave_active && ts <= wave_pos_lo + 31) {
-      const char* kt = sk + buf * C::kTileBytes;
-      const char* vt = sv + buf * C::kTileBytes;
-      f32x16 sc[2];
+  // One tile of work on stage ST (already in LDS).
+  auto compute_tile = [&](int ts, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr int KOFF = ST * C::kStageBytes;
+    f32x16 sc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-        const int key = kb * 32 + i32;
-        const char* krow = kt + key * C::kRowBytes;
-        const int sw = lds_swz(key);
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    }
+    if constexpr (KS == 8) {
+      u32x4 kw[8];
+      ds_read_b128_x8<KOFF>(ka, kw);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kw = *reinterpret_cast<const u32x4*>(krow + (((2 * ks + g2) ^ sw) << 4));
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qf[ks], sc[kb], 0, 0, 0);
-        }
-      }
-      if (ts + C::kTile - 1 > wave_pos_lo || ts + C::kTile > kv1) {
-        const int pos = prefix + qi;
+      for (int ks = 0; ks < 8; ++ks)
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[0], 0, 0, 0);
+      ds_read_b128_x8<KOFF + 32 * C::kRowBytes>(ka, kw);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < 8; ++ks)
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[1], 0, 0, 0);
+    } else {
+      u32x4 kw[4];
+      ds_read_b128_x4<KOFF>(ka, kw);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-            if (key >= kv1 || key > pos) sc[kb][r] = -INFINITY;
-          }
-      }
-      float mx = sc[0][0];
+      for (int ks = 0; ks < 4; ++ks)
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[0], 0, 0, 0);
+      ds_read_b128_x4<KOFF + 32 * C::kRowBytes>(ka, kw);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
-      // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
-      // (weights stay <= 2^8); numerator and denominator share the same reference, so the
-      // result is unchanged.
-      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-        m = mnew;
-      }
-      const float muse = m == -INFINITY ? 0.f : m;
-      float psum = 0.f;
+      for (int ks = 0; ks < 4; ++ks)
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[1], 0, 0, 0);
+    }
+    if (ts + C::kTile - 1 > wave_pos_lo || ts + C::kTile > kv1) {
+      const int pos = prefix + qi;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sc[kb][r] = fast_exp2(fmaf(sc[kb][r], c, -muse));
-          psum += sc[kb][r];
+          const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          if (key >= kv1 || key > pos) sc[kb][r] = -INFINITY;
         }
-      l += psum;
+    }
+    float mx = sc[0][0];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int kb = kk >> 1, rb = 8 * (kk & 1);
-        u32x4 pw = {pack_bf16x2(sc[kb][rb + 0], sc[kb][rb + 1]),
-                    pack_bf16x2(sc[kb][rb + 2], sc[kb][rb + 3]),
-                    pack_bf16x2(sc[kb][rb + 4], sc[kb][rb + 5]),
-                    pack_bf16x2(sc[kb][rb + 6], sc[kb][rb + 7])};
-        const bf16x8 pf = as_bf16x8(pw);
-        const int key1 = 16 * kk + v_key_off;
-        const int key2 = key1 + 8;
-        const char* vrow1 = vt + key1 * C::kRowBytes + v_byte_in_chunk;
-        const char* vrow2 = vt + key2 * C::kRowBytes + v_byte_in_chunk;
-        const int sw1 = lds_swz(key1), sw2 = lds_swz(key2);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
+    // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
+    // (weights stay <= 2^8); numerator and denominator share the same reference, so the
+    // result is unchanged.
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+      m = mnew;
+    }
+    const float muse = m == -INFINITY ? 0.f : m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[kb][r] = fast_exp2(fmaf(sc[kb][r], c, -muse));
+        psum += sc[kb][r];
+      }
+    l += psum;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kb = kk >> 1, rb = 8 * (kk & 1);
+      u32x4 pw = {pack_bf16x2(sc[kb][rb + 0], sc[kb][rb + 1]),
+                  pack_bf16x2(sc[kb][rb + 2], sc[kb][rb + 3]),
+                  pack_bf16x2(sc[kb][rb + 4], sc[kb][rb + 5]),
+                  pack_bf16x2(sc[kb][rb + 6], sc[kb][rb + 7])};
+      const bf16x8 pf = as_bf16x8(pw);
+      constexpr int VOFF = KOFF;        // + 16*kk key rows, applied below per k-step
+      if constexpr (NB == 4) {
+        u32x2 r[8];
+        switch (kk) {
+          case 0: ds_read_b64_tr_b16_x8<VOFF>(va, r); break;
+          case 1: ds_read_b64_tr_b16_x8<VOFF + 16 * C::kRowBytes>(va, r); break;
+          case 2: ds_read_b64_tr_b16_x8<VOFF + 32 * C::kRowBytes>(va, r); break;
+          default: ds_read_b64_tr_b16_x8<VOFF + 48 * C::kRowBytes>(va, r); break;
+        }
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          const int chunk = (32 * n + v_d) >> 3;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vrow1 + ((chunk ^ sw1) << 4)));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vrow2 + ((chunk ^ sw2) << 4)));
-          const u32x4 vw = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
+          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+        }
+      } else {
+        u32x2 r[4];
+        switch (kk) {
+          case 0: ds_read_b64_tr_b16_x4<VOFF>(va, r); break;
+          case 1: ds_read_b64_tr_b16_x4<VOFF + 16 * C::kRowBytes>(va, r); break;
+          case 2: ds_read_b64_tr_b16_x4<VOFF + 32 * C::kRowBytes>(va, r); break;
+          default: ds_read_b64_tr_b16_x4<VOFF + 48 * C::kRowBytes>(va, r); break;
+        }
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
           acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
         }
       }
     }
+  };
+  // a wave skips tiles whose every key lies after every one of its rows
+  auto active = [&](int ts) { return wave_active && ts <= wave_pos_lo + 31; };
+
+  // Two stages: while a tile is consumed from one, the next streams into the other; block ids
+  // of the tile after that are read meanwhile. Unrolled by two so the stage is a constant.
+  const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
+  int ids0[P], ids1[P];
+  block_ids(kv0, ids0);
+  issue_tile(kv0, ids0, 0);
+  if (ntiles > 1) block_ids(kv0 + C::kTile, ids1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    const int ts = kv0 + it * C::kTile;
+    if (it + 1 < ntiles) {
+      issue_tile(ts + C::kTile, ids1, 1);
+      if (it + 2 < ntiles) block_ids(ts + 2 * C::kTile, ids0);
+    }
+    if (active(ts)) compute_tile(ts, std::integral_constant<int, 0>());
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) {
+      issue_tile(ts + 2 * C::kTile, ids0, 0);
+      if (it + 3 < ntiles) block_ids(ts + 3 * C::kTile, ids1);
+    }
+    if (active(ts + C::kTile)) compute_tile(ts + C::kTile, std::integral_constant<int, 1>());
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
