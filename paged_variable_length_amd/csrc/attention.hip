@@ -423,18 +423,21 @@ __device__ __forceinline__ int lds_swz(int key) {
     return ((key & 3) << 1) | ((key >> 2) & 1);
 }
 
-// N (4 or 8) LDS reads of one kind at lane addresses a[i] plus the byte offset OFF, issued
-// together and completed before returning. One asm block: the compiler cannot tell that these
-// reads never touch the stage the direct loads are filling and would otherwise wait for those
-// loads first. The block ends with lgkmcnt(0), so nothing it issued is outstanding afterwards.
-#define PA_LDS_READ8(OP, T)                                                                   \
+// Batches of N (4 or 8) LDS reads of one kind at lane addresses a[i] plus the byte offset
+// OFF, written as asm: the compiler cannot tell that these reads never touch the stage the
+// direct loads are filling and would otherwise wait for those loads before each read.
+// `_issue` only issues the reads. `lds_wait<K>` then waits until at most K LDS operations are
+// outstanding and ties the batch's registers, so nothing reads them before the data arrived.
+// LDS operations complete in issue order, so with K = the number of reads issued after a
+// batch, that batch is complete; other counted operations in between only make the wait
+// stronger. The compiler's own waits stay valid: extra outstanding operations are older.
+#define PA_LDS_READ(OP, T)                                                                    \
   template <int OFF>                                                                          \
-  __device__ __forceinline__ void OP##_x8(const uint32_t (&a)[8], T (&r)[8]) {                \
+  __device__ __forceinline__ void OP##_x8_issue(const uint32_t (&a)[8], T (&r)[8]) {          \
     asm volatile(#OP " %0, %8 offset:%16\n\t" #OP " %1, %9 offset:%16\n\t"                   \
                  #OP " %2, %10 offset:%16\n\t" #OP " %3, %11 offset:%16\n\t"                  \
                  #OP " %4, %12 offset:%16\n\t" #OP " %5, %13 offset:%16\n\t"                  \
-                 #OP " %6, %14 offset:%16\n\t" #OP " %7, %15 offset:%16\n\t"                  \
-                 "s_waitcnt lgkmcnt(0)"                                                       \
+                 #OP " %6, %14 offset:%16\n\t" #OP " %7, %15 offset:%16"                      \
                  : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]),           \
                    "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])                                      \
                  : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),          \
@@ -442,17 +445,31 @@ __device__ __forceinline__ int lds_swz(int key) {
                  : "memory");                                                                 \
   }                                                                                           \
   template <int OFF>                                                                          \
-  __device__ __forceinline__ void OP##_x4(const uint32_t (&a)[4], T (&r)[4]) {                \
+  __device__ __forceinline__ void OP##_x4_issue(const uint32_t (&a)[4], T (&r)[4]) {          \
     asm volatile(#OP " %0, %4 offset:%8\n\t" #OP " %1, %5 offset:%8\n\t"                     \
-                 #OP " %2, %6 offset:%8\n\t" #OP " %3, %7 offset:%8\n\t"                      \
-                 "s_waitcnt lgkmcnt(0)"                                                       \
+                 #OP " %2, %6 offset:%8\n\t" #OP " %3, %7 offset:%8"                          \
                  : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])                         \
                  : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(OFF)                       \
                  : "memory");                                                                 \
   }
-PA_LDS_READ8(ds_read_b128, u32x4)
-PA_LDS_READ8(ds_read_b64_tr_b16, u32x2)
-#undef PA_LDS_READ8
+PA_LDS_READ(ds_read_b128, u32x4)
+PA_LDS_READ(ds_read_b64_tr_b16, u32x2)
+#undef PA_LDS_READ
+
+template <int K, typename T>
+__device__ __forceinline__ void lds_wait(T (&r)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                 "+v"(r[6]), "+v"(r[7])
+               : "n"(K)
+               : "memory");
+}
+template <int K, typename T>
+__device__ __forceinline__ void lds_wait(T (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])
+               : "n"(K)
+               : "memory");
+}
 
 typedef __attribute__((address_space(4))) const int32_t cint32;
 
@@ -583,25 +600,29 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
     }
     if constexpr (KS == 8) {
-      u32x4 kw[8];
-      ds_read_b128_x8<KOFF>(ka, kw);
+      u32x4 kw0[8], kw1[8];
+      ds_read_b128_x8_issue<KOFF>(ka, kw0);
+      ds_read_b128_x8_issue<KOFF + 32 * C::kRowBytes>(ka, kw1);
+      lds_wait<8>(kw0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[0], 0, 0, 0);
-      ds_read_b128_x8<KOFF + 32 * C::kRowBytes>(ka, kw);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw0[ks]), qf[ks], sc[0], 0, 0, 0);
+      lds_wait<0>(kw1);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[1], 0, 0, 0);
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw1[ks]), qf[ks], sc[1], 0, 0, 0);
     } else {
-      u32x4 kw[4];
-      ds_read_b128_x4<KOFF>(ka, kw);
+      u32x4 kw0[4], kw1[4];
+      ds_read_b128_x4_issue<KOFF>(ka, kw0);
+      ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(ka, kw1);
+      lds_wait<4>(kw0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[0], 0, 0, 0);
-      ds_read_b128_x4<KOFF + 32 * C::kRowBytes>(ka, kw);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw0[ks]), qf[ks], sc[0], 0, 0, 0);
+      lds_wait<0>(kw1);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[ks]), qf[ks], sc[1], 0, 0, 0);
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw1[ks]), qf[ks], sc[1], 0, 0, 0);
     }
     if (ts + C::kTile - 1 > wave_pos_lo || ts + C::kTile > kv1) {
       const int pos = prefix + qi;
@@ -640,43 +661,42 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         psum += sc[kb][r];
       }
     l += psum;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    constexpr int VOFF = KOFF;                                      // va includes the V part
+    constexpr int NR = 2 * NB;                                      // tr reads per k-step
+    typedef u32x2 VR[NR];
+    VR vr0, vr1;
+    auto v_issue = [&](auto kk_tag, VR& r) {
+      constexpr int KK = decltype(kk_tag)::value;
+      if constexpr (NR == 8)
+        ds_read_b64_tr_b16_x8_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
+      else
+        ds_read_b64_tr_b16_x4_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
+    };
+    auto pv = [&](int kk, VR& r) {
       const int kb = kk >> 1, rb = 8 * (kk & 1);
       u32x4 pw = {pack_bf16x2(sc[kb][rb + 0], sc[kb][rb + 1]),
                   pack_bf16x2(sc[kb][rb + 2], sc[kb][rb + 3]),
                   pack_bf16x2(sc[kb][rb + 4], sc[kb][rb + 5]),
                   pack_bf16x2(sc[kb][rb + 6], sc[kb][rb + 7])};
       const bf16x8 pf = as_bf16x8(pw);
-      constexpr int VOFF = KOFF;        // + 16*kk key rows, applied below per k-step
-      if constexpr (NB == 4) {
-        u32x2 r[8];
-        switch (kk) {
-          case 0: ds_read_b64_tr_b16_x8<VOFF>(va, r); break;
-          case 1: ds_read_b64_tr_b16_x8<VOFF + 16 * C::kRowBytes>(va, r); break;
-          case 2: ds_read_b64_tr_b16_x8<VOFF + 32 * C::kRowBytes>(va, r); break;
-          default: ds_read_b64_tr_b16_x8<VOFF + 48 * C::kRowBytes>(va, r); break;
-        }
 #pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
-          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
-        }
-      } else {
-        u32x2 r[4];
-        switch (kk) {
-          case 0: ds_read_b64_tr_b16_x4<VOFF>(va, r); break;
-          case 1: ds_read_b64_tr_b16_x4<VOFF + 16 * C::kRowBytes>(va, r); break;
-          case 2: ds_read_b64_tr_b16_x4<VOFF + 32 * C::kRowBytes>(va, r); break;
-          default: ds_read_b64_tr_b16_x4<VOFF + 48 * C::kRowBytes>(va, r); break;
-        }
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
-          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
-        }
+      for (int n = 0; n < NB; ++n) {
+        const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
       }
-    }
+    };
+    v_issue(std::integral_constant<int, 0>(), vr0);
+    v_issue(std::integral_constant<int, 1>(), vr1);
+    lds_wait<NR>(vr0);
+    pv(0, vr0);
+    v_issue(std::integral_constant<int, 2>(), vr0);
+    lds_wait<NR>(vr1);
+    pv(1, vr1);
+    v_issue(std::integral_constant<int, 3>(), vr1);
+    lds_wait<NR>(vr0);
+    pv(2, vr0);
+    lds_wait<0>(vr1);
+    pv(3, vr1);
   };
   // a wave skips tiles whose every key lies after every one of its rows
   auto active = [&](int ts) { return wave_active && ts <= wave_pos_lo + 31; };
