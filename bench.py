@@ -12,7 +12,7 @@ Headline (`value`): decode KV GB/s on the 64-sequence MHA decode batch (Hq = Hkv
 out, the block-table entries read) over the measured step time. Secondary workloads in the same
 JSON line: GQA decode at block sizes 16 and 64, the packed varlen causal prefill (TFLOP/s) and
 the mixed unified step (both). `roofline` covers the attention launch of the headline workload,
-timed with HIP events on the launch stream, with the L2/MALL flushed between launches.
+timed with HIP events on the launch stream, with L2/MALL evicted (a 1 GiB read) between launches.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--only] [--no-cpu-baseline]
 """
@@ -92,11 +92,14 @@ class Runner:
         self.cu = torch.from_numpy(self.cu_host).to(dev)
         self.ctx = torch.from_numpy(self.ctx_host).to(dev)
         self.bt = torch.from_numpy(w.block_table).to(dev)
-        cap_t, cap_c = max(self.num_tasks, 1), max(self.num_combines, 1)
-        self.pin_t = [torch.zeros((cap_t, 8), dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.pin_c = [torch.zeros((cap_c, 8), dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.dev_t = [torch.zeros((cap_t, 8), dtype=torch.int32, device=dev) for _ in range(2)]
-        self.dev_c = [torch.zeros((cap_c, 8), dtype=torch.int32, device=dev) for _ in range(2)]
+        # one pinned and one device buffer per slot: task rows, then combine rows, so a
+        # single copy carries the whole table
+        self.cap_t, self.cap_c = max(self.num_tasks, 1), max(self.num_combines, 1)
+        rows = self.cap_t + self.cap_c
+        self.pin = [torch.zeros((rows, 8), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev = [torch.zeros((rows, 8), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream()      # default priority
+        self.copy_ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.slot_ev = [None, None]
         nbytes = pa.workspace_bytes(self.num_partials, w.head_dim)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -107,32 +110,39 @@ class Runner:
         self.step_no = 0
 
     def build_table(self, k):
-        """Host table for slot k into pinned memory, then an async copy to the device slot."""
-        pa = self.pa
+        """Host table for slot k into pinned memory, then one async copy to the device slot on
+        the copy stream, so it overlaps the kernels of the step before."""
+        pa, torch = self.pa, self.torch
         if self.slot_ev[k] is not None:
             self.slot_ev[k].synchronize()      # the slot's previous copy and kernels are done
-        t = pa.build_task_table(self.params, self.cu_host, self.ctx_host, self.pin_t[k].numpy(),
-                                self.pin_c[k].numpy(), with_balance=False)
+        pin = self.pin[k].numpy()
+        t = pa.build_task_table(self.params, self.cu_host, self.ctx_host, pin[:self.cap_t],
+                                pin[self.cap_t:], with_balance=False)
         nt, nc = len(t.tasks), len(t.combines)
-        self.dev_t[k][:nt].copy_(self.pin_t[k][:nt], non_blocking=True)
-        if nc:
-            self.dev_c[k][:nc].copy_(self.pin_c[k][:nc], non_blocking=True)
+        n = self.cap_t + nc
+        with torch.cuda.stream(self.copy_stream):
+            self.dev[k][:n].copy_(self.pin[k][:n], non_blocking=True)
+            self.copy_ev[k].record()
         return nt, nc, t.num_partials
 
     def launch(self, k, nt, nc, nparts, ev_pair=None):
-        """Cache write, then the attention launch (bracketed by ev_pair if given)."""
+        """Cache write, then the attention launch (bracketed by ev_pair if given), on the
+        current stream once slot k's table copy has landed."""
         pa, v = self.pa, self.vals
+        self.torch.cuda.current_stream().wait_event(self.copy_ev[k])
+        tasks = self.dev[k][:nt]
+        combines = self.dev[k][self.cap_t:self.cap_t + nc]
         pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt, self.cu,
                              self.ctx)
         if ev_pair is not None:
             ev_pair[0].record()
         if self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
-                                 self.dev_t[k][:nt], self.dev_c[k][:nc], nparts, self.ws, self.out)
+                                 tasks, combines, nparts, self.ws, self.out)
         else:
             pa.paged_attn_varlen_prefill(v["q"], v["k_pages"], v["v_pages"], self.bt, self.cu,
-                                         self.ctx, self.scale, self.dev_t[k][:nt],
-                                         self.dev_c[k][:nc], nparts, self.ws, self.out)
+                                         self.ctx, self.scale, tasks, combines, nparts, self.ws,
+                                         self.out)
         if ev_pair is not None:
             ev_pair[1].record()
 
@@ -142,9 +152,9 @@ class Runner:
         self.step_no += 1
         nt, nc, nparts = self.build_table(k)
         self.launch(k, nt, nc, nparts)
-        ev = self.torch.cuda.Event()
-        ev.record()
-        self.slot_ev[k] = ev
+        if self.slot_ev[k] is None:
+            self.slot_ev[k] = self.torch.cuda.Event()
+        self.slot_ev[k].record()
 
     def timed_steps(self, steps, warmup):
         torch = self.torch
@@ -160,16 +170,17 @@ class Runner:
     def launch_times(self, launches, flush):
         """Average duration of the attention launch, from HIP events recorded on the current
         stream (the stream the library launches on). The table is built once; each iteration
-        flushes L2/MALL with a 512 MiB write, rewrites the cache, and brackets the attention
-        launch. Nothing synchronises the host inside the loop, so the queue stays full and the
-        events time the GPU work, not host launch latency."""
+        evicts L2/MALL by reading a 1 GiB buffer (a read leaves no dirty lines whose
+        write-back would land on the timed kernel), rewrites the cache, and brackets the
+        attention launch. Nothing synchronises the host inside the loop, so the queue stays
+        full and the events time the GPU work, not host launch latency."""
         torch = self.torch
         torch.cuda.synchronize()
         nt, nc, nparts = self.build_table(0)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(launches)]
         for e in evs:
-            flush.fill_(1)
+            flush.sum()
             self.launch(0, nt, nc, nparts, e)
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in evs]
@@ -253,6 +264,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dec-split", type=int, default=None, help="override decode key split")
+    ap.add_argument("--pf-kv-split", type=int, default=None, help="override prefill key split")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -260,9 +273,14 @@ def main():
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    for tl in TILING.values():
+        if args.dec_split is not None and "dec_split" in tl:
+            tl["dec_split"] = args.dec_split
+        if args.pf_kv_split is not None and "pf_kv_split" in tl:
+            tl["pf_kv_split"] = args.pf_kv_split
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(2**28, dtype=torch.float32, device="cuda")     # 1 GiB, read to evict
 
     if args.calibrate_copy:
         src = torch.ones(2**28, dtype=torch.float32, device="cuda")   # 1 GiB

@@ -51,11 +51,6 @@ extern "C" int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu) {
 
 namespace {
 
-struct Emitted {
-  int64_t load;
-  pa_task task;
-};
-
 int check_params(const pa_params* p) {
   if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
     return set_error(PA_ERR_SHAPE, "query heads (%d) must be a positive multiple of kv heads (%d)",
@@ -105,15 +100,19 @@ int64_t tile_pairs(int64_t e0, int64_t e1, int64_t kv0, int64_t kv1) {
 template <class EmitF, class CombF>
 void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
                EmitF&& emit, CombF&& combine, int64_t* num_partials) {
-  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  // parameters in locals: the stores of emitted records could otherwise alias them
+  const int32_t Hq = p->num_q_heads, Hkv = p->num_kv_heads, G = Hq / Hkv;
+  const int32_t dec_split = p->dec_split, q_tile = p->pf_q_tile, kv_split = p->pf_kv_split;
+  const int64_t weight = p->decode_weight;
   int64_t parts = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t ql = cu[s + 1] - cu[s];
-    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
+    const int32_t keys = ctx[s];
+    const int64_t prefix = static_cast<int64_t>(keys) - ql;
     if (ql == 1) {
       // decode: key splits of dec_split per kv head, all G query heads in one task
-      const int32_t nsplit = static_cast<int32_t>(ceil_div(ctx[s], p->dec_split));
-      for (int32_t g = 0; g < p->num_kv_heads; ++g) {
+      const int32_t nsplit = static_cast<int32_t>(ceil_div(keys, dec_split));
+      for (int32_t g = 0; g < Hkv; ++g) {
         int64_t first = -1;
         if (nsplit > 1) {
           first = parts;
@@ -121,20 +120,20 @@ void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_
           combine(pa_combine{s, 0, 1, g * G, G, static_cast<int32_t>(first), nsplit, 0});
         }
         for (int32_t k = 0; k < nsplit; ++k) {
-          const int32_t kv0 = k * p->dec_split;
-          const int32_t kv1 = std::min(ctx[s], kv0 + p->dec_split);
+          const int32_t kv0 = k * dec_split;
+          const int32_t kv1 = std::min(keys, kv0 + dec_split);
           const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * G) : -1;
-          emit(int64_t(kv1 - kv0) * G * p->decode_weight,
+          emit(int64_t(kv1 - kv0) * G * weight,
                pa_task{PA_TASK_DECODE, s, g, 0, 1, kv0, kv1, part});
         }
       }
     } else {
       // prefill: causal query tiles per query head, each split along its visible keys
-      for (int32_t h = 0; h < p->num_q_heads; ++h) {
-        for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
-          const int32_t rows = std::min(p->pf_q_tile, ql - r0);
+      for (int32_t h = 0; h < Hq; ++h) {
+        for (int32_t r0 = 0; r0 < ql; r0 += q_tile) {
+          const int32_t rows = std::min(q_tile, ql - r0);
           const int64_t lim = prefix + r0 + rows;  // keys visible to the tile's last row
-          const int64_t split = p->pf_kv_split > 0 ? p->pf_kv_split : lim;
+          const int64_t split = kv_split > 0 ? kv_split : lim;
           const int32_t nsplit = static_cast<int32_t>(ceil_div(lim, split));
           int64_t first = -1;
           if (nsplit > 1) {
@@ -191,32 +190,66 @@ void count(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t nu
   *np = parts;
 }
 
-// Stable order of `em` by load, descending: LSD radix sort (11-bit digits) on
-// (max_load - load), which keeps equal loads in emission order.
-void sort_by_load_desc(const std::vector<Emitted>& em, std::vector<uint32_t>& order) {
-  const size_t n = em.size();
-  int64_t mx = 0;
-  for (const Emitted& e : em) mx = std::max(mx, e.load);
-  static thread_local std::vector<uint32_t> tmp;
-  order.resize(n);
-  tmp.resize(n);
-  for (size_t i = 0; i < n; ++i) order[i] = static_cast<uint32_t>(i);
-  constexpr int kBits = 11;
-  constexpr uint64_t kMask = (1u << kBits) - 1;
-  std::vector<uint32_t> hist(size_t(1) << kBits);
-  for (int shift = 0; shift < 64 && (static_cast<uint64_t>(mx) >> shift) != 0; shift += kBits) {
-    std::fill(hist.begin(), hist.end(), 0u);
-    for (size_t i = 0; i < n; ++i) ++hist[(static_cast<uint64_t>(mx - em[order[i]].load) >> shift) & kMask];
+// Stable order of n loads, descending: an LSD radix sort on keys that hold (max_load - load)
+// above the emission index, so equal loads keep emission order and the sort moves plain 64-bit
+// words. The digits cover only the bits of max_load - min_load, at most 11 per pass. Returns the
+// buffer (`a` or `b`, n entries each) that holds the sorted keys; the low 32 bits of each key are
+// the emission index.
+//
+// Emission produces long runs of equal loads, so one bucket counter would take every increment
+// back to back; the input is cut into kWays interleaved ranges with counters of their own (equal
+// digits from an earlier range still land first, which keeps the sort stable).
+uint64_t* sort_by_load_desc(const int64_t* load, uint32_t n, int64_t mn, int64_t mx, uint64_t* a,
+                            uint64_t* b) {
+  for (uint32_t i = 0; i < n; ++i) a[i] = (static_cast<uint64_t>(mx - load[i]) << 32) | i;
+  const uint64_t span = static_cast<uint64_t>(mx - mn);
+  int bits = 0;
+  while (bits < 32 && (span >> bits) != 0) ++bits;
+  if (bits == 0) return a;
+  constexpr int kMaxBits = 11, kWays = 4;
+  const int passes = (bits + kMaxBits - 1) / kMaxBits;
+  const int width = (bits + passes - 1) / passes;
+  const uint64_t mask = (uint64_t(1) << width) - 1;
+  const uint32_t buckets = 1u << width;
+  static thread_local std::vector<uint32_t> hist_store;
+  hist_store.resize(size_t(kWays) << kMaxBits);
+  uint32_t* hist = hist_store.data();  // [bucket][way]
+  const uint32_t q = n / kWays;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = 32 + pass * width;
+    std::fill(hist, hist + size_t(kWays) * buckets, 0u);
+    for (uint32_t i = 0; i < q; ++i)
+      for (int w = 0; w < kWays; ++w) ++hist[((a[w * q + i] >> shift) & mask) * kWays + w];
+    for (uint32_t i = kWays * q; i < n; ++i) ++hist[((a[i] >> shift) & mask) * kWays + kWays - 1];
     uint32_t run = 0;
-    for (uint32_t& h : hist) {
-      const uint32_t c = h;
-      h = run;
+    for (uint32_t j = 0; j < kWays * buckets; ++j) {
+      const uint32_t c = hist[j];
+      hist[j] = run;
       run += c;
     }
-    for (size_t i = 0; i < n; ++i)
-      tmp[hist[(static_cast<uint64_t>(mx - em[order[i]].load) >> shift) & kMask]++] = order[i];
-    order.swap(tmp);
+    for (uint32_t i = 0; i < q; ++i)
+      for (int w = 0; w < kWays; ++w) {
+        const uint64_t k = a[w * q + i];
+        b[hist[((k >> shift) & mask) * kWays + w]++] = k;
+      }
+    for (uint32_t i = kWays * q; i < n; ++i) {
+      const uint64_t k = a[i];
+      b[hist[((k >> shift) & mask) * kWays + kWays - 1]++] = k;
+    }
+    std::swap(a, b);
   }
+  return a;
+}
+
+// Scratch of the calling thread, grown on demand and reused across calls.
+struct Scratch {
+  std::vector<int64_t> load;
+  std::vector<pa_task> task;
+  std::vector<uint64_t> key, tmp;
+};
+Scratch& scratch() {
+  static thread_local Scratch s;
+  return s;
 }
 
 }  // namespace
@@ -254,27 +287,54 @@ extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int
   if (nt > 0 && !tasks) return set_error(PA_ERR_NULL, "build_task_table: tasks is NULL");
   if (nc > 0 && !combines) return set_error(PA_ERR_NULL, "build_task_table: combines is NULL");
 
-  static thread_local std::vector<Emitted> em;
-  static thread_local std::vector<uint32_t> order;
-  em.clear();
-  em.reserve(static_cast<size_t>(nt));
-  int64_t nci = 0, parts = 0;
+  Scratch& sc = scratch();
+  if (sc.load.size() < static_cast<size_t>(nt)) {
+    sc.load.resize(nt);
+    sc.task.resize(nt);
+    sc.key.resize(nt);
+    sc.tmp.resize(nt);
+  }
+  int64_t* loads = sc.load.data();
+  pa_task* emitted = sc.task.data();
+  int64_t nti = 0, nci = 0, parts = 0;
+  int64_t mn = INT64_MAX, mx = 0;
   decompose(
-      p, cu, ctx, num_seqs, [&](int64_t load, const pa_task& t) { em.push_back(Emitted{load, t}); },
+      p, cu, ctx, num_seqs,
+      [&](int64_t load, const pa_task& t) {
+        if (nti < nt) {
+          loads[nti] = load;
+          emitted[nti] = t;
+          mn = std::min(mn, load);
+          mx = std::max(mx, load);
+        }
+        ++nti;
+      },
       [&](const pa_combine& c) {
         if (nci < nc) combines[nci] = c;
         ++nci;
       },
       &parts);
-  if (static_cast<int64_t>(em.size()) != nt || nci != nc || parts != np)
+  if (nti != nt || nci != nc || parts != np)
     return set_error(PA_ERR_SHAPE, "build_task_table: internal count mismatch");
-  sort_by_load_desc(em, order);
-  for (size_t i = 0; i < em.size(); ++i) tasks[i] = em[order[i]].task;
+  const uint64_t* order;
+  if (nt == 0 || static_cast<uint64_t>(mx - mn) < (uint64_t(1) << 32)) {
+    order = sort_by_load_desc(loads, static_cast<uint32_t>(nt), mn, mx, sc.key.data(),
+                              sc.tmp.data());
+  } else {
+    // loads spread over more than 2^32 (a 128-row tile over tens of millions of keys): a stable
+    // comparison sort of the emission indices instead of the packed keys
+    uint64_t* idx = sc.key.data();
+    for (int64_t i = 0; i < nt; ++i) idx[i] = static_cast<uint64_t>(i);
+    std::stable_sort(idx, idx + nt,
+                     [loads](uint64_t x, uint64_t y) { return loads[x] > loads[y]; });
+    order = idx;
+  }
+  for (int64_t i = 0; i < nt; ++i) tasks[i] = emitted[static_cast<uint32_t>(order[i])];
   if (balance) {
     const int32_t W = p->num_workers;
     std::vector<int64_t> snake(W, 0), modulo(W, 0);
-    for (size_t i = 0; i < em.size(); ++i) {
-      const int64_t ld = em[order[i]].load;
+    for (int64_t i = 0; i < nt; ++i) {
+      const int64_t ld = loads[static_cast<uint32_t>(order[i])];
       const size_t rnd = i / W, pos = i % W;
       snake[rnd % 2 == 0 ? pos : W - 1 - pos] += ld;
       modulo[i % W] += ld;

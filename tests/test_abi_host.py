@@ -78,6 +78,23 @@ def test_task_table_bit_exact_random(seed):
                    decode_weight=int(rng.integers(1, 4)))
 
 
+def test_task_table_many_distinct_loads():
+    # prefill tiles over long prefixes give loads spread over ~2^22, so the sort takes several
+    # digit passes; ties between heads must keep emission order
+    q = [200, 1, 130, 1, 77]
+    ctx = [40000, 9000, 25000, 3, 4000]
+    compare_tables(q, ctx, hq=4, hkv=2, bs=64, dec_split=192, pf_q_tile=64, pf_kv_split=0,
+                   num_workers=7, decode_weight=3)
+
+
+def test_task_table_loads_wider_than_32_bits():
+    # a 128-row tile behind a 2^25-key prefix has a load above 2^32, next to a one-key decode
+    q = [128, 1, 1]
+    ctx = [2**25 + 128, 1, 70]
+    compare_tables(q, ctx, hq=2, hkv=1, bs=16, dec_split=64, pf_q_tile=128, pf_kv_split=0,
+                   num_workers=3)
+
+
 def test_task_table_errors_match_oracle():
     cases = [
         (dict(hq=2, hkv=1, bs=12), [1], [5], _abi.PA_ERR_BLOCK_SIZE),
