@@ -36,13 +36,41 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16"]
+# Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
+# splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
+# query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
 TILING = {
-    "decode_mha_bf16": dict(dec_split=512),
-    "decode_gqa_bf16_bs16": dict(dec_split=512),
-    "decode_gqa_bf16_bs64": dict(dec_split=512),
+    "decode_mha_bf16": dict(dec_split=1024),
+    "decode_gqa_bf16_bs16": dict(dec_split=8192),
+    "decode_gqa_bf16_bs64": dict(dec_split=8192),
     "prefill_varlen_bf16": dict(pf_q_tile=128, pf_kv_split=0),
-    "mixed_bf16": dict(dec_split=512, pf_q_tile=128, pf_kv_split=8192),
+    "mixed_bf16": dict(dec_split=4096, pf_q_tile=128, pf_kv_split=0),
 }
+KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
+
+
+def counter_traffic(workload, tiling):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, if it was taken on the current kernel source and tiling (else
+    None). The summary's header records the source hash, the tiling and the calibrated bytes."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    meta = {}
+    for line in open(path):
+        if line.startswith("# ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            meta[k.strip()] = v.strip()
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if meta.get("kernel source sha256") != src or meta.get("tiling") != json.dumps(tiling,
+                                                                                   sort_keys=True):
+        return None
+    try:
+        rd, wr = (float(x) for x in meta["launch traffic bytes (read, write)"].split(","))
+    except (KeyError, ValueError):
+        return None
+    return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr, "source": os.path.relpath(path, ROOT)}
 
 
 def algorithmic_work(w):
@@ -266,6 +294,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dec-split", type=int, default=None, help="override decode key split")
     ap.add_argument("--pf-kv-split", type=int, default=None, help="override prefill key split")
+    ap.add_argument("--pf-q-tile", type=int, default=None, help="override prefill query tile")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -278,6 +307,8 @@ def main():
             tl["dec_split"] = args.dec_split
         if args.pf_kv_split is not None and "pf_kv_split" in tl:
             tl["pf_kv_split"] = args.pf_kv_split
+        if args.pf_q_tile is not None and "pf_q_tile" in tl:
+            tl["pf_q_tile"] = args.pf_q_tile
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     flush = torch.ones(2**28, dtype=torch.float32, device="cuda")     # 1 GiB, read to evict
@@ -323,6 +354,7 @@ def main():
         cpu = cpu_baseline(args.workload)
     import synth
     wl = synth.make_workload(args.workload)
+    traffic = counter_traffic(args.workload, head["tiling"])
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -342,7 +374,9 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, **TILING[args.workload]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_detail": traffic,
                      "kernel": "paged_attn_decode launch (decode_kernel + combine_kernel)",
                      "bytes_per_launch": wk["bytes"],
                      "launch_ms_avg": head["attn_launch_ms_avg"],

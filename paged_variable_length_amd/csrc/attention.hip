@@ -17,9 +17,11 @@
 // through LDS at the end and write either the output row or an fp32 partial.
 //
 // Prefill body (MFMA-bound). A task is (sequence, query head, up to 128 query rows, key
-// range). 64-key K/V tiles are gathered through the block table into double-buffered LDS;
-// each wave owns 32 query rows, computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16
-// MFMAs, and applies the causal mask only on tiles that cross the diagonal.
+// range). 64-key K and V tiles are gathered through the block table into two LDS buffers
+// each; each wave owns 32 query rows, computes S^T = K Q^T and O^T += V^T P^T with 32x32x16
+// bf16 MFMAs, and applies the causal mask only on tiles that cross the diagonal. The tile
+// loop is software-pipelined: the scores of tile j+1 are formed while the exponentials of
+// tile j are, and the value product of tile j runs beside the maximum of tile j+1.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -385,15 +387,16 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
 //                  d-row i of block n <-> d = 32*n + i.
 //   O^T C-layout:  acc[n] reg r = O[row i32][d = 32*n + 8*(r/4) + 4*g2 + r%4].
 // K/V tiles reach LDS by direct global->LDS loads (16 bytes per lane, 1 KiB per wave
-// instruction) into two stages of [K tile | V tile]. Rows are stored unpadded with the 16-byte
-// chunks of key row k permuted by XOR with lds_swz(k), so the K reads and the transposed V
-// reads spread over the banks.
+// instruction) into [K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1]; K runs two tiles
+// ahead of its use and V one. Rows are stored unpadded with the 16-byte chunks of key row k
+// permuted by XOR with lds_swz(k), so the K reads and the transposed V reads spread over the
+// banks.
 // V^T operands come from ds_read_b64_tr_b16: within each 16-lane group, lane j = 4r + c
 // returns element c of the 8-byte segments addressed by lanes r, 4+r, 8+r, 12+r. With lane k
 // of the group addressing key kbase + k/4, d = d0 + 4*(k%4), lane j receives the four keys
 // kbase .. kbase+3 at d = d0 + j -- a column of V, as the MFMA operand needs.
-// Every lane-dependent LDS address is computed once per task; stage, key block and k-step
-// enter as instruction offsets, so the tile loop does no address arithmetic for LDS.
+// Lane-dependent LDS addresses are computed once per task; buffer, key block and k-step
+// enter as instruction offsets or as one XOR on a single base register.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
@@ -401,10 +404,9 @@ struct PrefillCfg {
   static constexpr int kRowBytes = D * 2;                           // one bf16 key row
   static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
   static constexpr int kTileBytes = kTile * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes;                // K tile then V tile
   static constexpr int kKeysPerLoad = 1024 / kRowBytes;             // keys per wave load
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;       // per tensor per tile
-  static constexpr size_t kSmemBytes = 2 * static_cast<size_t>(kStageBytes);
+  static constexpr size_t kSmemBytes = 4 * static_cast<size_t>(kTileBytes);  // 2 K + 2 V
 };
 
 // XOR pattern of the 16-byte chunks of key row `key` (a permutation of the row's chunks).
@@ -424,7 +426,7 @@ __device__ __forceinline__ int lds_swz(int key) {
 }
 
 // Batches of N (4 or 8) LDS reads of one kind at lane addresses a[i] plus the byte offset
-// OFF, written as asm: the compiler cannot tell that these reads never touch the stage the
+// OFF, written as asm: the compiler cannot tell that these reads never touch the buffer the
 // direct loads are filling and would otherwise wait for those loads before each read.
 // `_issue` only issues the reads. `lds_wait<K>` then waits until at most K LDS operations are
 // outstanding and ties the batch's registers, so nothing reads them before the data arrived.
@@ -473,12 +475,37 @@ __device__ __forceinline__ void lds_wait(T (&r)[4]) {
 
 typedef __attribute__((address_space(4))) const int32_t cint32;
 
+// Causal mask of one 32-key block of S^T scores: register r holds key offset
+// BASE + 8*(r/4) + r%4 (plus the lane's own offset, folded into lim); offsets >= lim become
+// -inf. Written as compare/select pairs on VCC so no lane masks pile up in scalar registers.
+template <int OFF>
+__device__ __forceinline__ float mask_one(float x, int lim, float ninf) {
+  asm("v_cmp_lt_i32_e32 vcc, %2, %1\n\tv_cndmask_b32_e32 %0, %3, %0, vcc"
+      : "+v"(x)
+      : "v"(lim), "n"(OFF), "v"(ninf)
+      : "vcc");
+  return x;
+}
+template <int BASE>
+__device__ __forceinline__ void mask_block(f32x16& s, int lim) {
+  const float ninf = -INFINITY;
+  s[0] = mask_one<BASE + 0>(s[0], lim, ninf);    s[1] = mask_one<BASE + 1>(s[1], lim, ninf);
+  s[2] = mask_one<BASE + 2>(s[2], lim, ninf);    s[3] = mask_one<BASE + 3>(s[3], lim, ninf);
+  s[4] = mask_one<BASE + 8>(s[4], lim, ninf);    s[5] = mask_one<BASE + 9>(s[5], lim, ninf);
+  s[6] = mask_one<BASE + 10>(s[6], lim, ninf);   s[7] = mask_one<BASE + 11>(s[7], lim, ninf);
+  s[8] = mask_one<BASE + 16>(s[8], lim, ninf);   s[9] = mask_one<BASE + 17>(s[9], lim, ninf);
+  s[10] = mask_one<BASE + 18>(s[10], lim, ninf); s[11] = mask_one<BASE + 19>(s[11], lim, ninf);
+  s[12] = mask_one<BASE + 24>(s[12], lim, ninf); s[13] = mask_one<BASE + 25>(s[13], lim, ninf);
+  s[14] = mask_one<BASE + 26>(s[14], lim, ninf); s[15] = mask_one<BASE + 27>(s[15], lim, ninf);
+}
+
 template <int D>
 __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   typedef PrefillCfg<D> C;
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int NB = D / 32;   // 32-row d blocks of O^T
   constexpr int P = C::kLoadsPerWave;
+  constexpr int NR = 2 * NB;   // transposed V reads per k-step of the PV product
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i32 = lane & 31, g2 = lane >> 5;
   // task fields and per-sequence scalars are wave-uniform; readfirstlane lets the compiler
@@ -498,7 +525,6 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int qi = r0 + 32 * wave + i32;              // this lane's query row (sequence-relative)
   const bool row_ok = qi < r0 + rows;
-  const bool wave_active = 32 * wave_u < rows;
   const int wave_pos_lo = prefix + r0 + 32 * wave_u;  // position of the wave's first row
   const float c = a.scale_log2;
 
@@ -516,16 +542,17 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
 
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pages) + kvh * head_stride;
+  const char* kbase = static_cast<const char*>(a.k_pages) + kvh * head_stride * 2;
+  const char* vbase = static_cast<const char*>(a.v_pages) + kvh * head_stride * 2;
   cint32* bt = (cint32*)(a.block_table + static_cast<size_t>(s) * a.max_blocks);
 
-  // ---- lane-constant LDS addresses (stage 0; stage, key block and k-step are offsets)
+  // ---- LDS: [K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1], one 64-key tile each.
+  // Lane-constant addresses point into buffer 0 of each kind; buffer, key block and k-step
+  // enter as instruction offsets.
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-  uint32_t ka[KS];                          // K row i32, chunk 2*ks + g2
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    ka[ks] = lds0 + i32 * C::kRowBytes + (((2 * ks + g2) ^ lds_swz<D>(i32)) << 4);
+  // K row i32, chunk 2*ks + g2. The row base is a multiple of 256 bytes and k-step ks only
+  // flips chunk bits 1..3, so the address of k-step ks is ka0 ^ (ks << 5).
+  uint32_t ka0 = lds0 + i32 * C::kRowBytes + ((g2 ^ lds_swz<D>(i32)) << 4);
   const int gq = lane >> 4, jq = lane & 15;
   const int v_key = 4 * g2 + (jq >> 2);     // key of this lane's segment (+ 16*kk, + 8)
   const int v_d = 16 * (gq & 1) + 4 * (jq & 3);
@@ -535,50 +562,52 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int key = v_key + 8 * hf;
-      va[2 * n + hf] = lds0 + C::kTileBytes + key * C::kRowBytes +
+      va[2 * n + hf] = lds0 + 2 * C::kTileBytes + key * C::kRowBytes +
                        ((((32 * n + v_d) >> 3) ^ lds_swz<D>(key)) << 4) + 8 * (jq & 1);
     }
-  // ---- direct-load addressing. A wave's piece i covers kKeysPerLoad keys starting at a
-  // multiple of kKeysPerLoad, all in one block, so it needs one wave-uniform block id (a
-  // scalar load through the constant address space). Within a block the key's slot is
-  // (ts & (bs-1)) + (key_in_tile & (bs-1)) for 64-aligned tiles, so the lane part is constant.
-  uint32_t dma_off[P];                      // lane byte offset inside the (block, kv head) page
-  int dma_key[P];                           // lane's key within the tile
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const int key = (wave_u * P + i) * C::kKeysPerLoad + lane / C::kChunks;
-    const int chunk = (lane % C::kChunks) ^ lds_swz<D>(key);
-    dma_key[i] = key;
-    dma_off[i] = (key & (bs - 1)) * C::kRowBytes + chunk * 16;
-  }
-  auto block_ids = [&](int ts, int (&ids)[P]) {
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int kp = min(ts + (wave_u * P + i) * C::kKeysPerLoad, kv1 - 1);
-      ids[i] = bt[kp >> a.bs_shift];
-    }
+  // ---- direct-load addressing. Each wave loads 16 consecutive keys of every tile
+  // (P pieces of kKeysPerLoad keys). Tiles start at multiples of 64 keys and blocks hold at
+  // least 16 keys, so those 16 keys lie in one block: one wave-uniform block id per tile (a
+  // scalar load through the constant address space). Within the block the key's slot is
+  // (ts & (bs-1)) + (key_in_tile & (bs-1)), so the lane part of the offset is constant.
+  // Piece i of a wave starts kKeysPerLoad*i keys (1 KiB) after piece 0 and the swizzle of its
+  // keys differs from piece 0's in the low chunk bits only: its lane offset is
+  // (dma0 ^ (swizzle difference << 4)) + 1024*i, the last term an instruction offset.
+  const int key0 = wave_u * P * C::kKeysPerLoad + lane / C::kChunks;
+  uint32_t dma0 = (key0 & (bs - 1)) * C::kRowBytes +
+                        (((lane % C::kChunks) ^ lds_swz<D>(key0)) << 4);
+  auto dma_off = [&](int i) -> uint32_t {
+    return dma0 ^ ((lds_swz<D>(key0 + i * C::kKeysPerLoad) ^ lds_swz<D>(key0)) << 4);
+  };
+  const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
+  // block id of this wave's keys in tile `tile`; keys past the range are clamped, so any tile
+  // number is safe
+  auto block_id = [&](int tile) -> int {
+    const int kp = min(kv0 + tile * C::kTile + wave_u * P * C::kKeysPerLoad, kv1 - 1);
+    return bt[kp >> a.bs_shift];
   };
   // Keys past kv1 (last tile only) are read from key kv1-1 instead (valid memory, finite
-  // values); they are masked in the scores.
-  auto issue_tile = [&](int ts, const int (&ids)[P], int stage) {
+  // values); they are masked in the scores. `which` 0 loads K into K buffer `buf`, 1 loads V.
+  auto issue = [&](int tile, int id, int which, int buf) {
+    const int ts = kv0 + tile * C::kTile;
     const bool full = ts + C::kTile <= kv1;
-    const size_t tile_slot = static_cast<size_t>(ts & (bs - 1)) * C::kRowBytes;
+    const char* page = (which ? vbase : kbase) + static_cast<size_t>(id) * block_stride * 2;
+    char* dst0 = smem + (2 * which + buf) * C::kTileBytes + wave_u * P * 1024;
+    const uint32_t tile_slot = static_cast<uint32_t>(ts & (bs - 1)) * C::kRowBytes;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const size_t page = static_cast<size_t>(ids[i]) * block_stride * 2;
-      uint32_t off = dma_off[i];
-      size_t base = page + tile_slot;
-      if (!full) {
-        const int kabs = min(ts + dma_key[i], kv1 - 1);
-        base = page;
-        off = (kabs & (bs - 1)) * C::kRowBytes + (dma_off[i] & (C::kRowBytes - 1));
+      for (int i = 0; i < P; ++i)
+        __builtin_amdgcn_global_load_lds(page + tile_slot + dma_off(i) + i * 1024,
+                                         (__attribute__((address_space(3))) void*)(dst0 + i * 1024),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int kabs = min(ts + key0 + i * C::kKeysPerLoad, kv1 - 1);
+        __builtin_amdgcn_global_load_lds(
+            page + (kabs & (bs - 1)) * C::kRowBytes + (dma_off(i) & (C::kRowBytes - 1)),
+            (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16, 0, 0);
       }
-      char* dst = smem + stage * C::kStageBytes + (wave_u * P + i) * 1024;
-      const char* ksrc = reinterpret_cast<const char*>(kbase) + base + off;
-      const char* vsrc = reinterpret_cast<const char*>(vbase) + base + off;
-      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(dst + C::kTileBytes),
-                                       16, 0, 0);
     }
   };
 
@@ -589,80 +618,101 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // One tile of work on stage ST (already in LDS).
-  auto compute_tile = [&](int ts, auto stage_tag) {
-    constexpr int ST = decltype(stage_tag)::value;
-    constexpr int KOFF = ST * C::kStageBytes;
-    f32x16 sc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-    }
-    if constexpr (KS == 8) {
-      u32x4 kw0[8], kw1[8];
-      ds_read_b128_x8_issue<KOFF>(ka, kw0);
-      ds_read_b128_x8_issue<KOFF + 32 * C::kRowBytes>(ka, kw1);
-      lds_wait<8>(kw0);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw0[ks]), qf[ks], sc[0], 0, 0, 0);
-      lds_wait<0>(kw1);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw1[ks]), qf[ks], sc[1], 0, 0, 0);
-    } else {
-      u32x4 kw0[4], kw1[4];
-      ds_read_b128_x4_issue<KOFF>(ka, kw0);
-      ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(ka, kw1);
-      lds_wait<4>(kw0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw0[ks]), qf[ks], sc[0], 0, 0, 0);
-      lds_wait<0>(kw1);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw1[ks]), qf[ks], sc[1], 0, 0, 0);
-    }
-    if (ts + C::kTile - 1 > wave_pos_lo || ts + C::kTile > kv1) {
-      const int pos = prefix + qi;
+  // tiles this wave computes: those with a key at or before its last row's position
+  int nw = 0;
+  if (32 * wave_u < rows) {
+    const int last = wave_pos_lo + 31;     // keys <= last are visible to some row of the wave
+    nw = last < kv0 ? 0 : min(ntiles, (last - kv0) / C::kTile + 1);
+  }
+  nw = __builtin_amdgcn_readfirstlane(nw);
+
+  // ---- the three pieces of work on a tile. The loop runs them software-pipelined: the
+  // scores of tile j+1 are computed while the exponentials of tile j are formed, and the
+  // value product of tile j runs while the maximum of tile j+1 is taken, so the matrix cores
+  // and the vector ALUs work on independent data inside one wave. Each matrix instruction is
+  // followed by its share of the vector work, and sched_barrier keeps that order: the
+  // scheduler would otherwise gather all exponentials in one place.
+  u32x4 pw[4];                              // P of the current tile, bf16, per PV k-step
+  // Phase A: scores of the next tile (K buffer KB) into sn; exponentials of sc into pw.
+  auto phase_a = [&](auto kb_tag, auto do_qk, auto do_exp, f32x16 (&sn)[2], f32x16 (&sc)[2]) {
+    constexpr int KOFF = decltype(kb_tag)::value * C::kTileBytes;
+    constexpr bool QK = decltype(do_qk)::value, EXP = decltype(do_exp)::value;
+    const float muse = m == -INFINITY ? 0.f : m;
+    float psum = 0.f;
+    // word w of pw (0..15): exponentials of scores 2w, 2w+1 of key block w / 8
+    auto exp_word = [&](int w) {
+      const int kb = w >> 3, r = 2 * (w & 7);
+      const float e0 = fast_exp2(fmaf(sc[kb][r], c, -muse));
+      const float e1 = fast_exp2(fmaf(sc[kb][r + 1], c, -muse));
+      psum += e0;
+      psum += e1;
+      uint32_t word = pack_bf16x2(e0, e1);
+      // pins the word here: without it the exponentials sink towards their first use in
+      // the value product, after the matrix steps they are meant to overlap
+      asm volatile("" : "+v"(word));
+      pw[w >> 2][w & 3] = word;
+    };
+    if constexpr (QK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ts + kb * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          if (key >= kv1 || key > pos) sc[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
     }
-    float mx = sc[0][0];
+    // four matrix steps on key block KB_, k-steps KS0..KS0+3 from kw, each followed by one
+    // word of exponentials (words W0..W0+3)
+    auto group = [&](f32x16& acc_s, const u32x4 (&kw)[4], int ks0, int w0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
-    // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
-    // (weights stay <= 2^8); numerator and denominator share the same reference, so the
-    // result is unchanged.
-    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
-      l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-      m = mnew;
-    }
-    const float muse = m == -INFINITY ? 0.f : m;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[kb][r] = fast_exp2(fmaf(sc[kb][r], c, -muse));
-        psum += sc[kb][r];
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (QK)
+          acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[q]), qf[ks0 + q], acc_s, 0, 0, 0);
+        if constexpr (EXP) exp_word(w0 + q);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    l += psum;
-    constexpr int VOFF = KOFF;                                      // va includes the V part
-    constexpr int NR = 2 * NB;                                      // tr reads per k-step
+    };
+    u32x4 k0[4], k1[4];
+    if constexpr (KS == 8) {
+      const uint32_t kl[4] = {ka0, ka0 ^ (1u << 5), ka0 ^ (2u << 5), ka0 ^ (3u << 5)};
+      const uint32_t kh[4] = {ka0 ^ (4u << 5), ka0 ^ (5u << 5), ka0 ^ (6u << 5), ka0 ^ (7u << 5)};
+      if constexpr (QK) {
+        ds_read_b128_x4_issue<KOFF>(kl, k0);
+        ds_read_b128_x4_issue<KOFF>(kh, k1);
+        lds_wait<4>(k0);
+      }
+      group(sn[0], k0, 0, 0);
+      if constexpr (QK) {
+        ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kl, k0);
+        lds_wait<4>(k1);
+      }
+      group(sn[0], k1, 4, 4);
+      if constexpr (QK) {
+        ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kh, k1);
+        lds_wait<4>(k0);
+      }
+      group(sn[1], k0, 0, 8);
+      if constexpr (QK) lds_wait<0>(k1);
+      group(sn[1], k1, 4, 12);
+    } else {
+      const uint32_t kl[4] = {ka0, ka0 ^ (1u << 5), ka0 ^ (2u << 5), ka0 ^ (3u << 5)};
+      if constexpr (QK) {
+        ds_read_b128_x4_issue<KOFF>(kl, k0);
+        ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kl, k1);
+        lds_wait<4>(k0);
+      }
+      group(sn[0], k0, 0, 0);
+      if constexpr (QK) lds_wait<0>(k1);
+      group(sn[1], k1, 0, 4);
+      if constexpr (EXP) {
+#pragma unroll
+        for (int w = 8; w < 16; ++w) exp_word(w);
+      }
+    }
+    if constexpr (EXP) l += psum;
+  };
+  // Phase B: value product of the current tile (V buffer VB) with pw, and mask and maximum
+  // of the next tile's scores sn (starting at key ts_next); then the lazy rescale.
+  auto phase_b = [&](auto vb_tag, auto do_pv, auto do_max, f32x16 (&sn)[2], int ts_next) {
+    constexpr int VOFF = decltype(vb_tag)::value * C::kTileBytes;
+    constexpr bool PV = decltype(do_pv)::value, MAX = decltype(do_max)::value;
     typedef u32x2 VR[NR];
     VR vr0, vr1;
     auto v_issue = [&](auto kk_tag, VR& r) {
@@ -672,61 +722,123 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       else
         ds_read_b64_tr_b16_x4_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
     };
+    float mx = -INFINITY;
+    if constexpr (MAX) {
+      if (ts_next + C::kTile - 1 > wave_pos_lo || ts_next + C::kTile > kv1) {
+        // score (kb, r) holds key ts_next + 4*g2 + off with off = 32kb + 8(r/4) + r%4; it is
+        // visible iff key < min(kv1, pos + 1), i.e. off < lim
+        const int lim = min(kv1, prefix + qi + 1) - ts_next - 4 * g2;
+        mask_block<0>(sn[0], lim);
+        mask_block<32>(sn[1], lim);
+      }
+    }
+    // k-step kk: NB matrix steps, each followed by the maximum over a share of sn
+    constexpr int kMaxPer = 32 / (4 * NB);  // scores folded per matrix step
     auto pv = [&](int kk, VR& r) {
-      const int kb = kk >> 1, rb = 8 * (kk & 1);
-      u32x4 pw = {pack_bf16x2(sc[kb][rb + 0], sc[kb][rb + 1]),
-                  pack_bf16x2(sc[kb][rb + 2], sc[kb][rb + 3]),
-                  pack_bf16x2(sc[kb][rb + 4], sc[kb][rb + 5]),
-                  pack_bf16x2(sc[kb][rb + 6], sc[kb][rb + 7])};
-      const bf16x8 pf = as_bf16x8(pw);
+      const bf16x8 pf = as_bf16x8(pw[kk]);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+        if constexpr (PV) {
+          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
+          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+        }
+        if constexpr (MAX) {
+#pragma unroll
+          for (int i = 0; i < kMaxPer; ++i) {
+            const int v = (kk * NB + n) * kMaxPer + i;
+            mx = fmaxf(mx, sn[v >> 4][v & 15]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    v_issue(std::integral_constant<int, 0>(), vr0);
-    v_issue(std::integral_constant<int, 1>(), vr1);
-    lds_wait<NR>(vr0);
+    if constexpr (PV) {
+      v_issue(std::integral_constant<int, 0>(), vr0);
+      v_issue(std::integral_constant<int, 1>(), vr1);
+      lds_wait<NR>(vr0);
+    }
     pv(0, vr0);
-    v_issue(std::integral_constant<int, 2>(), vr0);
-    lds_wait<NR>(vr1);
+    if constexpr (PV) {
+      v_issue(std::integral_constant<int, 2>(), vr0);
+      lds_wait<NR>(vr1);
+    }
     pv(1, vr1);
-    v_issue(std::integral_constant<int, 3>(), vr1);
-    lds_wait<NR>(vr0);
+    if constexpr (PV) {
+      v_issue(std::integral_constant<int, 3>(), vr1);
+      lds_wait<NR>(vr0);
+    }
     pv(2, vr0);
-    lds_wait<0>(vr1);
+    if constexpr (PV) lds_wait<0>(vr1);
     pv(3, vr1);
+    if constexpr (MAX) {
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
+      // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
+      // (weights stay <= 2^8); numerator and denominator share the same reference, so the
+      // result is unchanged.
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+        m = mnew;
+      }
+    }
   };
-  // a wave skips tiles whose every key lies after every one of its rows
-  auto active = [&](int ts) { return wave_active && ts <= wave_pos_lo + 31; };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
 
-  // Two stages: while a tile is consumed from one, the next streams into the other; block ids
-  // of the tile after that are read meanwhile. Unrolled by two so the stage is a constant.
-  const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
-  int ids0[P], ids1[P];
-  block_ids(kv0, ids0);
-  issue_tile(kv0, ids0, 0);
-  if (ntiles > 1) block_ids(kv0 + C::kTile, ids1);
+  // ---- prologue: K0, V0 into buffers 0, K1 into K buffer 1; scores and maximum of tile 0
+  f32x16 sa[2], sb[2];
+  {
+    const int id0 = block_id(0);
+    issue(0, id0, 0, 0);
+    issue(0, id0, 1, 0);
+  }
+  int idV = block_id(1);                    // tile j+1 (its V is loaded in iteration j)
+  if (ntiles > 1) issue(1, idV, 0, 1);
+  int idK = block_id(2);                    // tile j+2 (its K is loaded in iteration j)
+  int idN = block_id(3);                    // tile j+3, read one iteration ahead
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    const int ts = kv0 + it * C::kTile;
-    if (it + 1 < ntiles) {
-      issue_tile(ts + C::kTile, ids1, 1);
-      if (it + 2 < ntiles) block_ids(ts + 2 * C::kTile, ids0);
+  if (nw > 0) {
+    phase_a(I0(), T_(), F_(), sa, sb);
+    phase_b(I0(), F_(), T_(), sa, kv0);
+  }
+
+  // ---- iteration j: wait for K(j+1) and V(j); load K(j+2) and V(j+1) into the buffers the
+  // previous iteration finished with; exponentials of j with scores of j+1; value product
+  // of j with mask and maximum of j+1. Unrolled by two so buffers and score sets are named
+  // statically: even j reads K buffer 1, V buffer 0, keeps scores of j in sa.
+  auto iteration = [&](int j, auto par_tag, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    constexpr int PAR = decltype(par_tag)::value;
+    // opaque redefinition: values derived from these bases (the per-k-step and per-piece
+    // addresses) are then recomputed where used instead of held in registers across the loop
+    asm volatile("" : "+v"(ka0), "+v"(dma0));
+    if (j > 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
-    if (active(ts)) compute_tile(ts, std::integral_constant<int, 0>());
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) {
-      issue_tile(ts + 2 * C::kTile, ids0, 0);
-      if (it + 3 < ntiles) block_ids(ts + 3 * C::kTile, ids1);
+    if (j + 2 < ntiles) issue(j + 2, idK, 0, PAR);
+    if (j + 1 < ntiles) issue(j + 1, idV, 1, 1 - PAR);
+    idV = idK;
+    idK = idN;
+    idN = block_id(j + 4);
+    // The scores of tile j+1 are formed even when this wave has no key to see there (its
+    // last tile, or past the range): the mask then sets all of them to -inf, whatever the K
+    // buffer holds, and the maximum leaves the running state unchanged. One code path keeps
+    // the accumulators in place across the loop.
+    if (j < nw) {
+      phase_a(std::integral_constant<int, 1 - PAR>(), T_(), T_(), snext, scur);
+      phase_b(std::integral_constant<int, PAR>(), T_(), T_(), snext, kv0 + (j + 1) * C::kTile);
     }
-    if (active(ts + C::kTile)) compute_tile(ts + C::kTile, std::integral_constant<int, 1>());
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    iteration(j, I0(), sa, sb);
+    if (j + 1 >= ntiles) break;
+    iteration(j + 1, I1(), sb, sa);
   }
 
   l += wave_shfl_xor(l, 32);
