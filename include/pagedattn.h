@@ -92,7 +92,7 @@ typedef struct pa_combine {
 
 /* Decomposition parameters.
  *   dec_split     keys per decode task; positive multiple of 64
- *   pf_q_tile     query rows per prefill task; 1..256
+ *   pf_q_tile     query rows per prefill task; 1..128 (four waves of 32 rows)
  *   pf_kv_split   keys per prefill task along the key axis; 0 = whole visible range, else a
  *                 positive multiple of 64
  *   num_workers   workers assumed by the balance report (e.g. CUs x resident workgroups)

@@ -70,8 +70,8 @@ def _check(p: Params, cu, ctx):
         raise TaskTableError(ERR_BLOCK_SIZE, "block size must be a power of two in [16, 256]")
     if p.dec_split < 64 or p.dec_split % 64:
         raise TaskTableError(ERR_SHAPE, "dec_split must be a positive multiple of 64")
-    if not 1 <= p.pf_q_tile <= 256:
-        raise TaskTableError(ERR_SHAPE, "pf_q_tile must lie in [1, 256]")
+    if not 1 <= p.pf_q_tile <= 128:
+        raise TaskTableError(ERR_SHAPE, "pf_q_tile must lie in [1, 128]")
     if p.pf_kv_split < 0 or p.pf_kv_split % 64:
         raise TaskTableError(ERR_SHAPE, "pf_kv_split must be 0 or a positive multiple of 64")
     if p.num_workers < 1 or p.decode_weight < 1:

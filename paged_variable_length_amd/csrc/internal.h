@@ -22,7 +22,7 @@ inline bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 // Largest query-head group one decode task covers (the MFMA column tile is 16 wide).
 constexpr int32_t kMaxGroup = 16;
 // Largest prefill query tile (rows per workgroup of the MFMA tile kernel).
-constexpr int32_t kMaxQTile = 256;
+constexpr int32_t kMaxQTile = 128;
 // Key granularity of split boundaries (decode chunks and prefill key tiles both divide it).
 constexpr int32_t kSplitQuantum = 64;
 

@@ -73,7 +73,7 @@ def test_task_table_bit_exact_random(seed):
     hkv = int(rng.choice([1, 2, 4]))
     hq = hkv * int(rng.choice([1, 2, 4, 8]))
     compare_tables(q, ctx, hq=hq, hkv=hkv, bs=int(rng.choice([16, 32, 64, 128, 256])),
-                   dec_split=64 * int(rng.integers(1, 6)), pf_q_tile=int(rng.integers(1, 257)),
+                   dec_split=64 * int(rng.integers(1, 6)), pf_q_tile=int(rng.integers(1, 129)),
                    pf_kv_split=64 * int(rng.integers(0, 5)), num_workers=int(rng.integers(1, 40)),
                    decode_weight=int(rng.integers(1, 4)))
 
@@ -101,7 +101,7 @@ def test_task_table_errors_match_oracle():
         (dict(hq=2, hkv=1, bs=48), [1], [5], _abi.PA_ERR_BLOCK_SIZE),
         (dict(hq=3, hkv=2, bs=16), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16, dec_split=100), [1], [5], _abi.PA_ERR_SHAPE),
-        (dict(hq=2, hkv=1, bs=16, pf_q_tile=257), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, pf_q_tile=129), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16, pf_kv_split=32), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16), [4], [3], _abi.PA_ERR_INPUT),
     ]
