@@ -214,6 +214,33 @@ class Runner:
         ms = [a.elapsed_time(b) for a, b in evs]
         return float(np.mean(ms)), float(np.min(ms))
 
+    def table_build_us(self, reps=20):
+        """Median host time of one task-table build into a pinned slot (no copy)."""
+        pin = self.pin[0].numpy()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            self.pa.build_task_table(self.params, self.cu_host, self.ctx_host, pin[:self.cap_t],
+                                     pin[self.cap_t:], with_balance=False)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts) * 1e6)
+
+    def reshape_times(self, launches, flush):
+        """Average duration of reshape_and_cache alone (HIP events on the launch stream, L2/MALL
+        evicted by a read between launches, as for the attention launch)."""
+        torch, pa, v = self.torch, self.pa, self.vals
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for a, b in evs:
+            flush.sum()
+            a.record()
+            pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt,
+                                 self.cu, self.ctx)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
     def finite(self):
         return bool(self.torch.isfinite(self.out).all())
 
@@ -278,6 +305,10 @@ def run(name, steps, warmup, with_launch_timing=True, flush=None):
         avg_ms, min_ms = r.launch_times(max(steps, 10), flush)
         res["attn_launch_ms_avg"] = round(avg_ms, 4)
         res["attn_launch_ms_min"] = round(min_ms, 4)
+        rs_ms = r.reshape_times(max(steps, 10), flush)
+        res["reshape_ms_avg"] = round(rs_ms, 4)
+        res["reshape_gbs"] = round(r.work["reshape_bytes"] / (rs_ms * 1e-3) / 1e9, 1)
+    res["table_build_us"] = round(r.table_build_us(), 1)
     del r
     import torch
     torch.cuda.empty_cache()
@@ -383,7 +414,8 @@ def main():
                      "launch_ms_min": head["attn_launch_ms_min"]},
         "cpu_baseline": cpu,
         "headline_detail": {k: head[k] for k in ("tasks", "combines", "balance_snake",
-                                                 "balance_modulo", "finite")},
+                                                 "balance_modulo", "finite", "table_build_us",
+                                                 "reshape_ms_avg", "reshape_gbs")},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
