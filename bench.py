@@ -35,7 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
-SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16"]
+SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
+             "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles"]
 # Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
 # splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
 # query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
@@ -45,6 +46,10 @@ TILING = {
     "decode_gqa_bf16_bs64": dict(dec_split=8192),
     "prefill_varlen_bf16": dict(pf_q_tile=128, pf_kv_split=0),
     "mixed_bf16": dict(dec_split=4096, pf_q_tile=128, pf_kv_split=0),
+    # 4-row drafts: verify tasks (one task reads each KV page once for 4 rows x 4 heads), and
+    # for comparison the same batch decomposed into prefill tiles (one per query head)
+    "verify_gqa_bf16": dict(dec_split=8192, verify_rows=4),
+    "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
@@ -105,7 +110,7 @@ class Runner:
         import paged_variable_length_amd as pa
         self.torch, self.pa = torch, pa
         self.name = name
-        self.w = w = synth.make_workload(name, seed)
+        self.w = w = synth.make_workload(name.split(":")[0], seed)   # "name:variant" tilings
         self.vals = synth.make_values(w, device="cuda", nan_sentinels=True)
         self.tiling = dict(TILING[name], num_workers=256 * 2)
         self.cu_host = pa.pack_seqlens(w.q_lens)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 enum pa_status {
   PA_OK = 0,
@@ -68,13 +68,18 @@ enum pa_status {
 
 enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 };
 
-enum pa_task_kind { PA_TASK_DECODE = 0, PA_TASK_PREFILL = 1 };
+enum pa_task_kind { PA_TASK_DECODE = 0, PA_TASK_PREFILL = 1, PA_TASK_VERIFY = 2 };
 
 /* One unit of attention work (8 x int32 = 32 bytes).
  *   kind    PA_TASK_DECODE: the single query row of sequence `seq`, all Hq/Hkv query heads of
  *           kv head `head`, keys [kv0, kv1).
  *           PA_TASK_PREFILL: query rows [q_row0, q_row0 + q_rows) (relative to the sequence's
  *           first packed row) of query head `head`, keys [kv0, kv1) minus the causal mask.
+ *           PA_TASK_VERIFY: all q_rows (2..16) rows of a short sequence (a speculative draft
+ *           being verified; XY-Serve page, section 2.2, "Meta-Attention" serves prefill,
+ *           decode and verify alike) for all Hq/Hkv query heads of kv head `head`, keys
+ *           [kv0, kv1) minus the causal mask; q_row0 = 0. Only paged_attn_varlen_prefill runs
+ *           these tasks.
  *   partial -1: the task sees all keys its rows need and writes `out` directly.
  *           >= 0: first workspace row of this task's partial result (one row per
  *           (query row, head) pair it covers); split_combine merges the partials. */
@@ -97,11 +102,15 @@ typedef struct pa_combine {
  *                 positive multiple of 64
  *   num_workers   workers assumed by the balance report (e.g. CUs x resident workgroups)
  *   decode_weight integer multiplier of decode-task loads (>= 1), to weigh bandwidth-bound
- *                 decode tasks against compute-bound prefill tiles in mixed batches */
+ *                 decode and verify tasks against compute-bound prefill tiles in mixed batches
+ *   verify_rows   0 (off) or 2..16: a sequence with 2 <= q_len <= verify_rows and
+ *                 (Hq/Hkv) * q_len <= 16 becomes verify tasks (key splits of dec_split per kv
+ *                 head, all its rows and heads in one task) instead of prefill tiles
+ *   reserved      must be 0 */
 typedef struct pa_params {
   int32_t num_q_heads, num_kv_heads, head_dim, block_size;
   int32_t dec_split, pf_q_tile, pf_kv_split, num_workers;
-  int32_t decode_weight, reserved[3];
+  int32_t decode_weight, verify_rows, reserved[2];
 } pa_params;
 
 /* ABI version of the loaded library (PA_ABI_VERSION when headers and library match). */
@@ -120,12 +129,13 @@ int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu_seqlens);
 /* Dynamic Decomposer (XY-Serve page, sections 2.2 and 4.4): build the load-sorted task table
  * for one step, on the host, from host copies of cu_seqlens_q [num_seqs+1] and
  * context_lens [num_seqs].
- *   Decode sequences (q_len 1) become ceil(ctx/dec_split) key splits per kv head; longer
+ *   Decode sequences (q_len 1) become ceil(ctx/dec_split) key splits per kv head; short
+ *   sequences selected by verify_rows become the same key splits as verify tasks; other
  *   sequences become causal query tiles of pf_q_tile rows per query head, each split along its
  *   visible keys by pf_kv_split. A task's load is its unmasked (row, key) pairs times the heads
- *   it covers (times decode_weight for decode tasks); tasks are stably sorted by load,
- *   descending. Partial rows are numbered in emission order (sequence, head, tile, split);
- *   groups with more than one split get one combine record each.
+ *   it covers (times decode_weight for decode and verify tasks); tasks are stably sorted by
+ *   load, descending. Partial rows are numbered in emission order (sequence, head, tile,
+ *   split); groups with more than one split get one combine record each.
  *   Outputs: tasks [tasks_cap], combines [combines_cap] (both caller-owned host buffers);
  *   *num_tasks, *num_combines, *num_partials always receive the required counts, so a call
  *   with capacity 0 sizes the buffers (then PA_ERR_CAPACITY). balance, if non-NULL, receives

@@ -8,6 +8,10 @@ ratio min/max of per-core load sums when the sorted tasks are dealt to the cores
 Readings taken where the pages leave the step open:
   * decode sequences (one query row) are split along the keys into pieces of ``dec_split``; one
     task covers all query heads of one kv head (grouped-query heads share the KV pages);
+  * short multi-row sequences (a draft being verified; the XY-Serve page's Meta-Attention serves
+    prefill, decode and verify alike) are split the same way when ``verify_rows`` allows it
+    (2 <= q_len <= verify_rows and G * q_len <= 16): one task covers all their rows and the G
+    query heads of one kv head, with the causal mask inside the task;
   * prefill rows are tiled by ``pf_q_tile`` per query head, and each tile's visible key range
     (causal, bottom-right aligned) is split into pieces of ``pf_kv_split`` (0 = no split);
   * tiles with no visible key are never emitted; every emitted split holds at least one key
@@ -28,6 +32,7 @@ Records (8 int32 each):
   task    = (kind, seq, head, q_row0, q_rows, kv0, kv1, partial)
             kind 0 = decode split, head = kv head (covers query heads head*G .. head*G+G-1)
             kind 1 = prefill tile, head = query head
+            kind 2 = verify split, head = kv head, q_rows = the sequence's rows, q_row0 = 0
   combine = (seq, q_row0, q_rows, head, heads, first_slot, n_slots, 0)
             partial row of split k, query row i, head j = first_slot + k*q_rows*heads + i*heads + j
 """
@@ -59,6 +64,7 @@ class Params:
     pf_kv_split: int = 0
     num_workers: int = 256
     decode_weight: int = 1
+    verify_rows: int = 0
 
 
 def _check(p: Params, cu, ctx):
@@ -76,6 +82,8 @@ def _check(p: Params, cu, ctx):
         raise TaskTableError(ERR_SHAPE, "pf_kv_split must be 0 or a positive multiple of 64")
     if p.num_workers < 1 or p.decode_weight < 1:
         raise TaskTableError(ERR_SHAPE, "num_workers and decode_weight must be >= 1")
+    if p.verify_rows != 0 and not 2 <= p.verify_rows <= 16:
+        raise TaskTableError(ERR_SHAPE, "verify_rows must be 0 or lie in [2, 16]")
     # cann-recipes-infer page, section 4.4: offsets start at 0 and increase strictly
     if len(cu) != len(ctx) + 1 or cu[0] != 0:
         raise TaskTableError(ERR_INPUT, "cu_seqlens must have N+1 entries starting at 0")
@@ -103,20 +111,25 @@ def build_task_table(p: Params, cu_seqlens_q, context_lens):
     for s in range(len(ctx)):
         ql = cu[s + 1] - cu[s]
         prefix = ctx[s] - ql
-        if ql == 1:
+        verify = 2 <= ql <= p.verify_rows and G * ql <= 16
+        if ql == 1 or verify:
+            kind = 2 if verify else 0
             nsplit = _ceil_div(ctx[s], p.dec_split)
             for g in range(p.num_kv_heads):
                 first = -1
                 if nsplit > 1:
                     first = num_partials
-                    num_partials += nsplit * G
-                    combines.append((s, 0, 1, g * G, G, first, nsplit, 0))
+                    num_partials += nsplit * ql * G
+                    combines.append((s, 0, ql, g * G, G, first, nsplit, 0))
                 for k in range(nsplit):
                     kv0 = k * p.dec_split
                     kv1 = min(ctx[s], kv0 + p.dec_split)
-                    part = first + k * G if nsplit > 1 else -1
-                    load = (kv1 - kv0) * G * p.decode_weight
-                    emitted.append((load, (0, s, g, 0, 1, kv0, kv1, part)))
+                    part = first + k * ql * G if nsplit > 1 else -1
+                    pairs = 0
+                    for i in range(ql):
+                        pairs += max(0, min(kv1, prefix + i + 1) - kv0)
+                    load = pairs * G * p.decode_weight
+                    emitted.append((load, (kind, s, g, 0, ql, kv0, kv1, part)))
         else:
             for h in range(p.num_q_heads):
                 for r0 in range(0, ql, p.pf_q_tile):

@@ -22,8 +22,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import _abi
-from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL, PagedAttnError,  # noqa: F401
-                   PaCombine, PaParams, PaTask, check, lib)
+from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F401
+                   PA_TASK_VERIFY, PagedAttnError, PaCombine, PaParams, PaTask, check, lib)
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
            "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
@@ -49,9 +49,10 @@ def pack_seqlens(lengths) -> np.ndarray:
 
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, dec_split=512, pf_q_tile=128,
-                pf_kv_split=0, num_workers=256, decode_weight=1) -> PaParams:
+                pf_kv_split=0, num_workers=256, decode_weight=1, verify_rows=0) -> PaParams:
     return PaParams(num_q_heads, num_kv_heads, head_dim, block_size, dec_split, pf_q_tile,
-                    pf_kv_split, num_workers, decode_weight, (ctypes.c_int32 * 3)(0, 0, 0))
+                    pf_kv_split, num_workers, decode_weight, verify_rows,
+                    (ctypes.c_int32 * 2)(0, 0))
 
 
 @dataclass

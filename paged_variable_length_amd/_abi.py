@@ -23,7 +23,8 @@ PA_BF16 = 0
 PA_FP32 = 1
 PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
-ABI_VERSION = 1
+PA_TASK_VERIFY = 2
+ABI_VERSION = 2
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -50,8 +51,8 @@ class PaCombine(ctypes.Structure):
 class PaParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("num_q_heads", "num_kv_heads", "head_dim", "block_size", "dec_split",
-                 "pf_q_tile", "pf_kv_split", "num_workers", "decode_weight")] + \
-               [("reserved", ctypes.c_int32 * 3)]
+                 "pf_q_tile", "pf_kv_split", "num_workers", "decode_weight", "verify_rows")] + \
+               [("reserved", ctypes.c_int32 * 2)]
 
 
 class PagedAttnError(RuntimeError):

@@ -80,7 +80,9 @@ __device__ __forceinline__ uint32_t pair_half(uint32_t a, uint32_t b, int odd) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode body, bf16. Lane map inside a wave: i16 = lane & 15, g4 = lane >> 4.
+// Decode body, bf16; also runs verify tasks (all R <= 16/G rows of a short sequence).
+// Score column i16 is (row i16 / G, head i16 % G) of the task's R*G columns; for decode R = 1
+// and the columns are the G query heads. Lane map inside a wave: i16 = lane & 15, g4 = lane >> 4.
 //   QK  (16x16x32): A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]
 //                   lane supplies token/head i16 and d = 32*ks + 8*g4 + 0..7.
 //   S   C-layout:   lane holds S[token 4*g4 + r][head i16], r = 0..3.
@@ -100,10 +102,12 @@ struct DecodeVRaw<64> {
   typedef u32x2 type;  // 4 bf16 along D
 };
 
+// Merge of the four waves' partial states per score column, then the output row or an fp32
+// partial. Column c is (row c / G, head c % G); rows are relative to packed row tok.
 template <int D>
 __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const pa_task& t,
-                                                       int tok, int G, float m, float l,
-                                                       const f32x4* acc, float* smem,
+                                                       int tok, int G, int ncol, float m,
+                                                       float l, const f32x4* acc, float* smem,
                                                        bool out_bf16) {
   constexpr int VEC = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -117,7 +121,7 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
     sm_m[wave * 16 + i16] = m;
     sm_l[wave * 16 + i16] = l;
   }
-  if (i16 < G) {
+  if (i16 < ncol) {
 #pragma unroll
     for (int n = 0; n < VEC; ++n)
 #pragma unroll
@@ -125,20 +129,23 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
   }
   __syncthreads();
   const int hq0 = t.head * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+    // a verify row may see no key of this split in any wave: weight 0 (m = -inf, l = 0)
+    const float Muse = M == -INFINITY ? 0.f : M;
     float L = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float wt = fast_exp2(sm_m[w * 16 + h] - M);
+      const float wt = fast_exp2(sm_m[w * 16 + h] - Muse);
       L += wt * sm_l[w * 16 + h];
       A += wt * sm_acc[(w * 16 + h) * D + d];
     }
     if (t.partial < 0) {
-      const size_t o = (static_cast<size_t>(tok) * a.num_q_heads + hq0 + h) * D + d;
+      const int row = h / G, hh = h - row * G;
+      const size_t o = (static_cast<size_t>(tok + row) * a.num_q_heads + hq0 + hh) * D + d;
       const float v = A / L;
       if (out_bf16)
         static_cast<__bf16*>(a.out)[o] = static_cast<__bf16>(v);
@@ -166,18 +173,26 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
   const int s = t.seq, kvh = t.head;
   const int tok = a.cu_seqlens ? a.cu_seqlens[s] : s;
   const int bs = a.block_size;
+  const int nrows = t.q_rows;                      // 1 for decode, the draft rows for verify
+  const int ncol = nrows * G;
+  const int row = i16 / G, hh = i16 - row * G;     // this lane's score column
 
   bf16x8 qf[KS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(tok) * a.num_q_heads + kvh * G + i16) * D + 8 * g4;
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) +
+        (static_cast<size_t>(tok + row) * a.num_q_heads + kvh * G + hh) * D + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (i16 < G) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+      if (i16 < ncol) v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
       qf[ks] = as_bf16x8(v);
     }
   }
+  // causal limit of this column: its row sits at position ctx - nrows + row and sees the keys
+  // before that position and the key at it (for decode: every key)
+  const int key_lim = a.context_lens[s] - nrows + row + 1;
+  const int lim_lo = a.context_lens[s] - nrows + 1;  // smallest limit over the task's rows
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
@@ -242,6 +257,15 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
         }
       }
     }
+    if (cs + 32 > lim_lo) {
+      // keys after a verify row's own position get no weight in that row's column (their
+      // values are finite: they lie below kv1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = cs + 16 * (e >> 2) + 4 * g4 + (e & 3);
+        if (key >= key_lim) sc[e >> 2][e & 3] = -INFINITY;
+      }
+    }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
@@ -272,7 +296,7 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
     }
   }
-  decode_merge_and_store<D>(a, t, tok, G, m, l, acc, smem, true);
+  decode_merge_and_store<D>(a, t, tok, G, ncol, m, l, acc, smem, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -374,7 +398,7 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
       for (int n = 0; n < VEC; ++n)
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[r][n], p[r], acc[n], 0, 0, 0);
   }
-  decode_merge_and_store<D>(a, t, tok, G, m, l, acc, smem, false);
+  decode_merge_and_store<D>(a, t, tok, G, G, m, l, acc, smem, false);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -900,10 +924,10 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
   __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
-  if (t.kind == PA_TASK_DECODE)
-    decode_task_bf16<D>(a, t, reinterpret_cast<float*>(smem));
-  else
+  if (t.kind == PA_TASK_PREFILL)
     prefill_task<D>(a, t, smem);
+  else
+    decode_task_bf16<D>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // One workgroup per combine record; each wave merges one (row, head) at a time.

@@ -69,7 +69,18 @@ int check_params(const pa_params* p) {
                      p->pf_kv_split, pa::kSplitQuantum);
   if (p->num_workers < 1 || p->decode_weight < 1)
     return set_error(PA_ERR_SHAPE, "num_workers and decode_weight must be >= 1");
+  if (p->verify_rows != 0 && (p->verify_rows < 2 || p->verify_rows > pa::kMaxGroup))
+    return set_error(PA_ERR_SHAPE, "verify_rows %d must be 0 or lie in [2, %d]", p->verify_rows,
+                     pa::kMaxGroup);
+  if (p->reserved[0] != 0 || p->reserved[1] != 0)
+    return set_error(PA_ERR_SHAPE, "pa_params.reserved must be zero");
   return PA_OK;
+}
+
+// A sequence of ql > 1 rows runs as verify tasks (all its rows and the G query heads of one kv
+// head in one task, as 16 score columns) when verify_rows allows it and G*ql columns fit.
+bool verify_seq(int32_t ql, int32_t G, int32_t verify_rows) {
+  return ql >= 2 && ql <= verify_rows && G * ql <= pa::kMaxGroup;
 }
 
 double ratio(const std::vector<int64_t>& v) {
@@ -93,8 +104,8 @@ int64_t tile_pairs(int64_t e0, int64_t e1, int64_t kv0, int64_t kv1) {
   return total;
 }
 
-// Emission order of the decomposition: sequences ascending; decode sequences give kv head,
-// then key split; prefill sequences give query head, then query tile, then key split.
+// Emission order of the decomposition: sequences ascending; decode and verify sequences give
+// kv head, then key split; prefill sequences give query head, then query tile, then key split.
 // `emit(load, task)` and `combine(record)` receive every item in that order, and the partial
 // rows are numbered in the same order.
 template <class EmitF, class CombF>
@@ -104,27 +115,31 @@ void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_
   const int32_t Hq = p->num_q_heads, Hkv = p->num_kv_heads, G = Hq / Hkv;
   const int32_t dec_split = p->dec_split, q_tile = p->pf_q_tile, kv_split = p->pf_kv_split;
   const int64_t weight = p->decode_weight;
+  const int32_t verify_rows = p->verify_rows;
   int64_t parts = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t ql = cu[s + 1] - cu[s];
     const int32_t keys = ctx[s];
     const int64_t prefix = static_cast<int64_t>(keys) - ql;
-    if (ql == 1) {
-      // decode: key splits of dec_split per kv head, all G query heads in one task
+    if (ql == 1 || verify_seq(ql, G, verify_rows)) {
+      // decode / verify: key splits of dec_split per kv head, all ql rows and G query heads
+      // in one task; its load counts the unmasked pairs of every row, times G
+      const int32_t kind = ql == 1 ? PA_TASK_DECODE : PA_TASK_VERIFY;
       const int32_t nsplit = static_cast<int32_t>(ceil_div(keys, dec_split));
+      const int64_t cols = static_cast<int64_t>(ql) * G;
       for (int32_t g = 0; g < Hkv; ++g) {
         int64_t first = -1;
         if (nsplit > 1) {
           first = parts;
-          parts += static_cast<int64_t>(nsplit) * G;
-          combine(pa_combine{s, 0, 1, g * G, G, static_cast<int32_t>(first), nsplit, 0});
+          parts += nsplit * cols;
+          combine(pa_combine{s, 0, ql, g * G, G, static_cast<int32_t>(first), nsplit, 0});
         }
         for (int32_t k = 0; k < nsplit; ++k) {
           const int32_t kv0 = k * dec_split;
           const int32_t kv1 = std::min(keys, kv0 + dec_split);
-          const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + int64_t(k) * G) : -1;
-          emit(int64_t(kv1 - kv0) * G * weight,
-               pa_task{PA_TASK_DECODE, s, g, 0, 1, kv0, kv1, part});
+          const int32_t part = nsplit > 1 ? static_cast<int32_t>(first + k * cols) : -1;
+          emit(tile_pairs(prefix + 1, prefix + ql, kv0, kv1) * G * weight,
+               pa_task{kind, s, g, 0, ql, kv0, kv1, part});
         }
       }
     } else {
@@ -165,12 +180,12 @@ void count(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t nu
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t ql = cu[s + 1] - cu[s];
     const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
-    if (ql == 1) {
+    if (ql == 1 || verify_seq(ql, static_cast<int32_t>(G), p->verify_rows)) {
       const int64_t nsplit = ceil_div(ctx[s], p->dec_split);
       t += nsplit * p->num_kv_heads;
       if (nsplit > 1) {
         c += p->num_kv_heads;
-        parts += nsplit * G * p->num_kv_heads;
+        parts += nsplit * G * ql * p->num_kv_heads;
       }
     } else {
       for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {

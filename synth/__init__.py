@@ -103,6 +103,12 @@ def _lengths(name: str, rng: np.random.Generator):
         q = np.concatenate([np.ones(200, np.int64), np.full(4, 512, np.int64)])
         ctx = np.concatenate([dec_ctx, prefix + 512])
         return q, ctx, 64, 8, 128, 128, "bf16", None
+    if name == "verify_gqa_bf16":
+        # the GQA decode batch with a 4-row draft per sequence (3 drafted tokens plus the last
+        # accepted one) verified in one step; contexts include the draft rows
+        u = rng.uniform(math.log(64.0), math.log(32768.0), size=256)
+        ctx = np.clip(np.floor(np.exp(u)), 64, 32768).astype(np.int64)
+        return np.full(256, 4, np.int64), ctx, 32, 8, 128, 16, "bf16", None
     raise KeyError(name)
 
 
@@ -114,6 +120,7 @@ WORKLOADS = {
     "decode_gqa_bf16_bs64": 3,
     "prefill_varlen_bf16": 4,
     "mixed_bf16": 5,
+    "verify_gqa_bf16": 6,
 }
 
 

@@ -64,18 +64,21 @@ def test_task_table_bit_exact_on_workloads(name):
                    bs=w.block_size, num_workers=512, **tiling)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_task_table_bit_exact_random(seed):
     rng = np.random.default_rng(100 + seed)
     n = int(rng.integers(1, 12))
-    q = [1 if rng.random() < 0.5 else int(rng.integers(2, 300)) for _ in range(n)]
+    q = [1 if rng.random() < 0.4 else
+         int(rng.integers(2, 9)) if rng.random() < 0.5 else int(rng.integers(2, 300))
+         for _ in range(n)]
     ctx = [qq + int(rng.integers(0, 700)) for qq in q]
     hkv = int(rng.choice([1, 2, 4]))
     hq = hkv * int(rng.choice([1, 2, 4, 8]))
     compare_tables(q, ctx, hq=hq, hkv=hkv, bs=int(rng.choice([16, 32, 64, 128, 256])),
                    dec_split=64 * int(rng.integers(1, 6)), pf_q_tile=int(rng.integers(1, 129)),
                    pf_kv_split=64 * int(rng.integers(0, 5)), num_workers=int(rng.integers(1, 40)),
-                   decode_weight=int(rng.integers(1, 4)))
+                   decode_weight=int(rng.integers(1, 4)),
+                   verify_rows=int(rng.choice([0, 2, 4, 8, 16])))
 
 
 def test_task_table_many_distinct_loads():
@@ -104,6 +107,8 @@ def test_task_table_errors_match_oracle():
         (dict(hq=2, hkv=1, bs=16, pf_q_tile=129), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16, pf_kv_split=32), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16), [4], [3], _abi.PA_ERR_INPUT),
+        (dict(hq=2, hkv=1, bs=16, verify_rows=1), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, verify_rows=17), [1], [5], _abi.PA_ERR_SHAPE),
     ]
     for kw, q, ctx, code in cases:
         hq, hkv, bs = kw.pop("hq"), kw.pop("hkv"), kw.pop("bs")
@@ -118,6 +123,14 @@ def test_task_table_errors_match_oracle():
     with pytest.raises(pa.PagedAttnError) as e:
         pa.build_task_table(pa.make_params(2, 1, 64, 16), np.array([0, 2, 2], np.int32), [5, 5])
     assert e.value.code == _abi.PA_ERR_INPUT
+
+
+def test_reserved_params_must_be_zero():
+    p = pa.make_params(2, 1, 64, 16)
+    p.reserved[1] = 3
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.build_task_table(p, np.array([0, 1], np.int32), np.array([5], np.int32))
+    assert e.value.code == _abi.PA_ERR_SHAPE
 
 
 def test_task_table_capacity_sizing():

@@ -245,6 +245,51 @@ def test_mixed_full_size_sampled():
     assert torch.isfinite(out).all()
 
 
+# ------------------------------------------------------------------------ verify (draft rows)
+@pytest.mark.parametrize("hq,hkv,bs", [(4, 1, 16), (8, 2, 64), (16, 8, 16), (8, 8, 128)])
+@pytest.mark.parametrize("dec_split", [64, 512])
+def test_verify_ragged(hq, hkv, bs, dec_split):
+    """Short multi-row sequences as verify tasks (all rows and the G heads of a kv head in one
+    task, causal inside the draft), with key splits and block tails; G*q_len <= 16 throughout
+    so every multi-row sequence is a verify task."""
+    G = hq // hkv
+    rmax = 16 // G
+    q = [min(r, rmax) for r in (2, 3, 4, 2, 8, 5, 16, 1, 2)]
+    ctx = [qq + p for qq, p in zip(q, [0, 1, 14, 61, 100, 300, 700, 513, 1030])]
+    w = synth.custom_workload(q, ctx, hq, hkv, 128, bs, seed=hq + bs + dec_split, spare_blocks=3)
+    plan_tasks = pa.build_task_table(
+        pa.make_params(hq, hkv, 128, bs, dec_split=dec_split, verify_rows=16),
+        pa.pack_seqlens(q), w.ctx_lens).tasks
+    assert {int(k) for k in plan_tasks[:, 0]} <= {0, 2} and 2 in set(plan_tasks[:, 0].tolist())
+    small_case(w, "varlen", dec_split=dec_split, verify_rows=16)
+
+
+def test_verify_with_decode_and_prefill_in_one_launch():
+    """Decode rows, verify drafts and prefill chunks in one table and one launch."""
+    q = [1, 4, 300, 1, 3, 2, 64]
+    ctx = [900, 4 + 1000, 300 + 50, 7, 3, 2 + 4095, 64 + 64]
+    w = synth.custom_workload(q, ctx, 32, 8, 128, 16, seed=77, spare_blocks=4)
+    small_case(w, "varlen", dec_split=256, pf_q_tile=128, pf_kv_split=128, verify_rows=4)
+
+
+def test_verify_full_size_sampled():
+    """The 256-sequence GQA batch with 4-row drafts as verify tasks in the benchmark's launch
+    configuration; every row of a seeded sample of sequences (shortest and longest included)."""
+    w = synth.make_workload("verify_gqa_bf16")
+    _announce(f"verify full N={w.num_seqs} T={w.num_tokens}")
+    rng = np.random.default_rng(3)
+    order = np.argsort(w.ctx_lens)
+    seqs = sorted(set([int(order[0]), int(order[-1])] +
+                      rng.choice(w.num_seqs, 30, replace=False).tolist()))
+    vals = synth.make_values(w, device=DEV)
+    h = host_subset(w, vals, seqs)
+    out, plan = run_gpu(w, vals, "varlen", dec_split=8192, verify_rows=4)
+    assert set(plan.table.tasks[:, 0].tolist()) == {2}
+    ref = oracle_subset(h, 1.0 / math.sqrt(w.head_dim))
+    check_close(to_np(out)[h["rows"]], ref, "bf16", "verify full")
+    assert torch.isfinite(out).all()
+
+
 # ------------------------------------------------------------------------ invariants on GPU
 def test_determinism_and_block_permutation_bitwise():
     q = [1, 130, 1, 40]

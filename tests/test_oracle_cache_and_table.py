@@ -80,6 +80,46 @@ def test_hand_derived_table():
     assert bal["snake"] == pytest.approx(78 / 134)
 
 
+def test_hand_derived_verify_table():
+    """A 3-row draft (ctx 100, so P = 97) with Hq=4, Hkv=2 (G=2), dec_split 64, verify_rows 4.
+    Derived by hand: per kv head g, splits [0,64) and [64,100), each covering rows 0..2 and
+    heads 2g, 2g+1 (6 columns); 2 splits -> one combine per g with 2*3*2 = 12 slots.
+      split [0,64): rows see 98, 99, 100 keys -> 64 each -> 192 pairs x G = 384
+      split [64,100): 34 + 35 + 36 = 105 pairs x G = 210
+    Emission g0s0, g0s1, g1s0, g1s1; stable descending order g0s0, g1s0, g0s1, g1s1."""
+    p = P(num_q_heads=4, num_kv_heads=2, verify_rows=4)
+    tasks, comb, npart, loads, _ = ot.build_task_table(p, [0, 3], [100])
+    assert tasks.tolist() == [
+        [2, 0, 0, 0, 3, 0, 64, 0],
+        [2, 0, 1, 0, 3, 0, 64, 12],
+        [2, 0, 0, 0, 3, 64, 100, 6],
+        [2, 0, 1, 0, 3, 64, 100, 18]]
+    assert loads.tolist() == [384, 384, 210, 210]
+    assert comb.tolist() == [[0, 0, 3, 0, 2, 0, 2, 0], [0, 0, 3, 2, 2, 12, 2, 0]]
+    assert npart == 24
+
+
+def test_verify_selection_rule():
+    """verify_rows 0 keeps prefill tiles; a q_len above verify_rows, or G*q_len above 16
+    columns, also stays a prefill tile; q_len 1 is always a decode task."""
+    cu, ctx = [0, 3], [100]
+    for p in (P(num_q_heads=4, num_kv_heads=2),                       # off
+              P(num_q_heads=4, num_kv_heads=2, verify_rows=2),        # 3 rows > 2
+              P(num_q_heads=16, num_kv_heads=2, verify_rows=4)):      # G*3 = 24 > 16
+        tasks, *_ = ot.build_task_table(p, cu, ctx)
+        assert set(tasks[:, 0].tolist()) == {1}
+    tasks, *_ = ot.build_task_table(P(num_q_heads=4, num_kv_heads=1, verify_rows=4), cu, ctx)
+    assert set(tasks[:, 0].tolist()) == {2}                          # G*3 = 12 columns
+    tasks, *_ = ot.build_task_table(P(num_q_heads=4, num_kv_heads=2, verify_rows=4), [0, 1], [9])
+    assert set(tasks[:, 0].tolist()) == {0}
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(verify_rows=1), cu, ctx)
+    assert e.value.code == ot.ERR_SHAPE
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(verify_rows=17), cu, ctx)
+    assert e.value.code == ot.ERR_SHAPE
+
+
 def test_balance_examples():
     """Four equal-shape decode tasks with loads 4,3,2,1 (x G) on two workers:
     modulo deals w0 = 4+2, w1 = 3+1; snake deals w0 = 4+1, w1 = 3+2."""
@@ -104,7 +144,7 @@ def coverage(p, cu, ctx, tasks):
     G = p.num_q_heads // p.num_kv_heads
     cnt = {}
     for kind, s, head, r0, rows, kv0, kv1, _ in tasks.tolist():
-        heads = range(head * G, head * G + G) if kind == 0 else [head]
+        heads = range(head * G, head * G + G) if kind in (0, 2) else [head]
         P_ = ctx[s] - (cu[s + 1] - cu[s])
         for h, i in itertools.product(heads, range(r0, r0 + rows)):
             for j in range(kv0, min(kv1, P_ + i + 1)):
@@ -112,31 +152,36 @@ def coverage(p, cu, ctx, tasks):
     return cnt
 
 
-@pytest.mark.parametrize("pf_kv_split,pf_q_tile,dec_split", [(0, 3, 64), (64, 5, 128), (128, 128, 64)])
-def test_coverage_and_load_identities(pf_kv_split, pf_q_tile, dec_split):
-    rng = np.random.default_rng(pf_kv_split + pf_q_tile)
-    q_lens = [1, 7, 1, 19, 1, 2]
+@pytest.mark.parametrize("pf_kv_split,pf_q_tile,dec_split,verify_rows",
+                         [(0, 3, 64, 0), (64, 5, 128, 0), (128, 128, 64, 0), (64, 5, 64, 4),
+                          (0, 128, 128, 8)])
+def test_coverage_and_load_identities(pf_kv_split, pf_q_tile, dec_split, verify_rows):
+    rng = np.random.default_rng(pf_kv_split + pf_q_tile + verify_rows)
+    q_lens = [1, 7, 1, 19, 1, 2, 4, 3]
     ctx = [int(rng.integers(1, 300)) if q == 1 else q + int(rng.integers(0, 200)) for q in q_lens]
     cu = oa.pack_lengths(q_lens).tolist()
     p = P(num_q_heads=4, num_kv_heads=2, pf_q_tile=pf_q_tile, pf_kv_split=pf_kv_split,
-          dec_split=dec_split, num_workers=3)
+          dec_split=dec_split, num_workers=3, verify_rows=verify_rows)
     tasks, comb, npart, loads, _ = ot.build_task_table(p, cu, ctx)
     cnt = coverage(p, cu, ctx, tasks)
     expect = {(s, h, i, j) for s in range(len(q_lens)) for h in range(4)
               for i in range(q_lens[s]) for j in range(ctx[s] - q_lens[s] + i + 1)}
     assert set(cnt) == expect and all(v == 1 for v in cnt.values())
-    # load identities: decode = sum ctx * Hq ; prefill = Hq * sum_i (P + i + 1)
+    # load identities: decode = sum ctx * Hq ; prefill and verify = Hq * sum_i (P + i + 1)
     dec = sum(l for t, l in zip(tasks.tolist(), loads) if t[0] == 0)
-    pre = sum(l for t, l in zip(tasks.tolist(), loads) if t[0] == 1)
+    multi = sum(l for t, l in zip(tasks.tolist(), loads) if t[0] in (1, 2))
     assert dec == sum(c * 4 for q, c in zip(q_lens, ctx) if q == 1)
-    assert pre == sum(4 * sum(c - q + i + 1 for i in range(q)) for q, c in zip(q_lens, ctx) if q > 1)
+    assert multi == sum(4 * sum(c - q + i + 1 for i in range(q))
+                        for q, c in zip(q_lens, ctx) if q > 1)
+    verify_seqs = {t[1] for t in tasks.tolist() if t[0] == 2}
+    assert verify_seqs == {s for s, q in enumerate(q_lens) if 2 <= q <= verify_rows}
     # every task has at least one unmasked pair
     assert np.all(loads > 0)
     # partial rows: each used exactly once, all below num_partials, consistent with combines
     used = []
     for kind, s, head, r0, rows, kv0, kv1, part in tasks.tolist():
         if part >= 0:
-            used += list(range(part, part + (2 if kind == 0 else rows)))
+            used += list(range(part, part + (rows * 2 if kind in (0, 2) else rows)))
     assert sorted(used) == list(range(npart))
     assert npart == sum(c[2] * c[4] * c[6] for c in comb.tolist())
 
