@@ -217,6 +217,7 @@ class Runner:
             self.launch(0, nt, nc, nparts, e)
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in evs]
+        self.last_launch_median = float(np.median(ms))
         return float(np.mean(ms)), float(np.min(ms))
 
     def table_build_us(self, reps=20):
@@ -270,6 +271,15 @@ def cpu_baseline(name, budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         threads = 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     for s in order:
         s = int(s)
         nblk = oa.blocks_needed(int(w.ctx_lens[s]), w.block_size)
@@ -294,7 +304,7 @@ def cpu_baseline(name, budget_s=12.0):
     del vals
     torch.cuda.empty_cache()
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "cores_available": affinity,
             "sample": f"{done_seqs} of {w.num_seqs} sequences of {name} (seeded order), "
                       f"fp64 NumPy cache scatter + attention, {spent:.1f} s"}
 
@@ -310,6 +320,7 @@ def run(name, steps, warmup, with_launch_timing=True, flush=None):
         avg_ms, min_ms = r.launch_times(max(steps, 10), flush)
         res["attn_launch_ms_avg"] = round(avg_ms, 4)
         res["attn_launch_ms_min"] = round(min_ms, 4)
+        res["attn_launch_ms_median"] = round(r.last_launch_median, 4)
         rs_ms = r.reshape_times(max(steps, 10), flush)
         res["reshape_ms_avg"] = round(rs_ms, 4)
         res["reshape_gbs"] = round(r.work["reshape_bytes"] / (rs_ms * 1e-3) / 1e9, 1)
@@ -331,6 +342,7 @@ def main():
     ap.add_argument("--dec-split", type=int, default=None, help="override decode key split")
     ap.add_argument("--pf-kv-split", type=int, default=None, help="override prefill key split")
     ap.add_argument("--pf-q-tile", type=int, default=None, help="override prefill query tile")
+    ap.add_argument("--decode-weight", type=int, default=None, help="override decode load weight")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -345,6 +357,8 @@ def main():
             tl["pf_kv_split"] = args.pf_kv_split
         if args.pf_q_tile is not None and "pf_q_tile" in tl:
             tl["pf_q_tile"] = args.pf_q_tile
+        if args.decode_weight is not None:
+            tl["decode_weight"] = args.decode_weight
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     flush = torch.ones(2**28, dtype=torch.float32, device="cuda")     # 1 GiB, read to evict
@@ -418,8 +432,10 @@ def main():
                      "launch_ms_avg": head["attn_launch_ms_avg"],
                      "launch_ms_min": head["attn_launch_ms_min"]},
         "cpu_baseline": cpu,
+        "gpu_over_cpu_baseline": round(value / cpu["value"], 1) if cpu else None,
         "headline_detail": {k: head[k] for k in ("tasks", "combines", "balance_snake",
                                                  "balance_modulo", "finite", "table_build_us",
+                                                 "attn_launch_ms_median",
                                                  "reshape_ms_avg", "reshape_gbs")},
         "secondary": secondary,
     }
