@@ -36,7 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
-             "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles"]
+             "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8"]
 # Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
 # splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
 # query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
@@ -50,6 +50,8 @@ TILING = {
     # for comparison the same batch decomposed into prefill tiles (one per query head)
     "verify_gqa_bf16": dict(dec_split=8192, verify_rows=4),
     "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
+    # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline)
+    "decode_mha_fp8": dict(dec_split=1024),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
@@ -78,27 +80,42 @@ def counter_traffic(workload, tiling):
     return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr, "source": os.path.relpath(path, ROOT)}
 
 
-def algorithmic_work(w):
+def algorithmic_work(w, fp8_pages=False):
     """Bytes the method must move and flops it must do, counting valid data only: every
-    visible K/V row once, q and out once, the block-table entries a sequence needs, its
+    visible K/V row once (one byte per element for fp8 pages, plus the K and V scale of each
+    (block, kv head) page read), q and out once, the block-table entries a sequence needs, its
     length; flops = 4*D per unmasked (query row, key) pair per query head."""
     esize = 2 if w.dtype == "bf16" else 4
-    e_kv = 2 * w.num_kv_heads * w.head_dim * esize
+    kv_size = 1 if fp8_pages else esize
+    e_kv = 2 * w.num_kv_heads * w.head_dim * kv_size
     ctx = w.ctx_lens.astype(np.int64)
     q = w.q_lens.astype(np.int64)
     nblk = (ctx + w.block_size - 1) // w.block_size
     T = int(q.sum())
+    scale_bytes = int(nblk.sum()) * w.num_kv_heads * 2 * 4 if fp8_pages else 0
     B = int(ctx.sum()) * e_kv + T * w.num_q_heads * w.head_dim * esize * 2 + int(nblk.sum()) * 4 \
-        + 4 * w.num_seqs
+        + 4 * w.num_seqs + scale_bytes
     P = ctx - q
     pairs = P * q + q * (q + 1) // 2                      # sum over rows i of (P + i + 1)
     dec = q == 1
     F_dec = int((pairs[dec]).sum()) * w.num_q_heads * 4 * w.head_dim
     F_pre = int((pairs[~dec]).sum()) * w.num_q_heads * 4 * w.head_dim
     B_dec = int(ctx[dec].sum()) * e_kv + int(dec.sum()) * w.num_q_heads * w.head_dim * esize * 2 \
-        + int(nblk[dec].sum()) * 4 + 4 * int(dec.sum())
+        + int(nblk[dec].sum()) * 4 + 4 * int(dec.sum()) + (scale_bytes if np.all(dec) else 0)
+    reshape = 2 * T * w.num_kv_heads * w.head_dim * esize * 2     # read the new rows, write them
+    if fp8_pages:
+        # the fp8 write reads the new rows once and reads and rewrites every valid row of each
+        # page it touches, plus that page's scale
+        rows = 0
+        for s in range(w.num_seqs):
+            p0, c = int(P[s]), int(ctx[s])
+            for lb in range(p0 // w.block_size, (c - 1) // w.block_size + 1):
+                rows += min(c, (lb + 1) * w.block_size) - lb * w.block_size
+        pages = int(((ctx - 1) // w.block_size - P // w.block_size + 1).sum())
+        reshape = 2 * w.num_kv_heads * (T * w.head_dim * esize + 2 * rows * w.head_dim
+                                        + pages * 8)
     return dict(bytes=B, flops_prefill=F_pre, flops_decode=F_dec, bytes_decode=B_dec,
-                reshape_bytes=2 * 2 * T * w.num_kv_heads * w.head_dim * esize)
+                reshape_bytes=reshape)
 
 
 class Runner:
@@ -112,6 +129,10 @@ class Runner:
         self.name = name
         self.w = w = synth.make_workload(name.split(":")[0], seed)   # "name:variant" tilings
         self.vals = synth.make_values(w, device="cuda", nan_sentinels=True)
+        self.fp8 = name.endswith("_fp8")
+        if self.fp8:                     # fp8 pages with page scales replace the bf16 pool
+            del self.vals["k_pages"], self.vals["v_pages"]
+            self.vals.update(synth.make_fp8_pages(w, device="cuda"))
         self.tiling = dict(TILING[name], num_workers=256 * 2)
         self.cu_host = pa.pack_seqlens(w.q_lens)
         self.ctx_host = w.ctx_lens.astype(np.int32)
@@ -139,7 +160,7 @@ class Runner:
         self.out = torch.empty_like(self.vals["q"])
         self.scale = 1.0 / math.sqrt(w.head_dim)
         self.decode_only = bool(np.all(w.q_lens == 1))
-        self.work = algorithmic_work(w)
+        self.work = algorithmic_work(w, self.fp8)
         self.step_no = 0
 
     def build_table(self, k):
@@ -158,6 +179,15 @@ class Runner:
             self.copy_ev[k].record()
         return nt, nc, t.num_partials
 
+    def write_cache(self):
+        pa, v = self.pa, self.vals
+        if self.fp8:
+            pa.reshape_and_cache_fp8(v["k_new"], v["v_new"], v["k_codes"], v["v_codes"],
+                                     v["k_scales"], v["v_scales"], self.bt, self.cu, self.ctx)
+        else:
+            pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt,
+                                 self.cu, self.ctx)
+
     def launch(self, k, nt, nc, nparts, ev_pair=None):
         """Cache write, then the attention launch (bracketed by ev_pair if given), on the
         current stream once slot k's table copy has landed."""
@@ -165,11 +195,14 @@ class Runner:
         self.torch.cuda.current_stream().wait_event(self.copy_ev[k])
         tasks = self.dev[k][:nt]
         combines = self.dev[k][self.cap_t:self.cap_t + nc]
-        pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt, self.cu,
-                             self.ctx)
+        self.write_cache()
         if ev_pair is not None:
             ev_pair[0].record()
-        if self.decode_only:
+        if self.fp8:
+            pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
+                                     v["v_scales"], self.bt, self.ctx, self.scale, tasks,
+                                     combines, nparts, self.ws, self.out)
+        elif self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
                                  tasks, combines, nparts, self.ws, self.out)
         else:
@@ -241,8 +274,7 @@ class Runner:
         for a, b in evs:
             flush.sum()
             a.record()
-            pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt,
-                                 self.cu, self.ctx)
+            self.write_cache()
             b.record()
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 enum pa_status {
   PA_OK = 0,
@@ -208,6 +208,41 @@ int paged_attn_varlen_prefill(const void* q, const void* k_pages, const void* v_
                               int32_t num_tasks, const pa_combine* combines_dev,
                               int32_t num_combines, int32_t num_partials, void* workspace,
                               size_t workspace_bytes, void* out, void* stream);
+
+/* fp8 KV pages (cann-recipes-infer page, section 5.2: values are scaled before they are
+ * stored, and each page keeps its scale factor, multiplied back on reading).
+ *   Page format: k_pages, v_pages uint8 [num_blocks, Hkv, block_size, D] holding OCP E4M3FN
+ *   codes; k_scales, v_scales float [num_blocks, Hkv], one scale per (block, kv head) page, always
+ *   a power of two; a cached value is code * scale.
+ *
+ * Cache write into fp8 pages: same rows and slots as reshape_and_cache (k_new, v_new bf16
+ * [num_tokens, Hkv, D]). Every page this step writes into is rescaled: its valid rows (those
+ * cached before, read as code * old scale, and this step's rows) set the page maximum M; the new
+ * scale is 2^k for the smallest integer k >= -120 with M <= 448 * 2^k (k = 0 when M = 0), and
+ * every valid row is stored again as the round-to-nearest-even E4M3FN code of value * 2^-k.
+ * Slots past the context are not written. Pages are caller-owned device memory; the scale of a
+ * page that holds no row before this step is not read.
+ *   Errors: as reshape_and_cache (no dtype argument: the inputs are bf16). */
+int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                          float* k_scales, float* v_scales, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, void* stream);
+
+/* Decode attention over fp8 pages: as paged_attn_decode with dtype PA_BF16 for q and out, each
+ * cached value read as code * page scale (an exact bf16 value, converted on load). The task
+ * table is one built with verify_rows = 0: the kernel runs PA_TASK_DECODE rows only, and the
+ * outputs of any other kind are not written. Errors as paged_attn_decode. */
+int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          float scale, const pa_task* tasks_dev, int32_t num_tasks,
+                          const pa_combine* combines_dev, int32_t num_combines,
+                          int32_t num_partials, void* workspace, size_t workspace_bytes,
+                          void* out, void* stream);
 
 /* Debug check of a host copy of a block table (cann-recipes-infer page, section 4.4, first
  * check: page ids inside [0, max_pages)): every entry a sequence needs,

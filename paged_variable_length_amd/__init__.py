@@ -27,6 +27,7 @@ from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
            "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
+           "reshape_and_cache_fp8", "paged_attn_decode_fp8",
            "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32"]
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -171,6 +172,30 @@ def reshape_and_cache(k_new, v_new, k_pages, v_pages, block_table, cu_seqlens_q,
     check(lib().reshape_and_cache(*args), "reshape_and_cache")
 
 
+def reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, k_scales, v_scales, block_table,
+                          cu_seqlens_q, context_lens, stream=None):
+    """Write packed bf16 rows [T, Hkv, D] into fp8 pages (uint8 [NB, Hkv, bs, D]) with float32
+    page scales [NB, Hkv], rescaling every page the step writes into (library kernel)."""
+    torch = _torch()
+    T, hkv, d = k_new.shape
+    nb, hkv2, bs, d2 = k_pages.shape
+    if (hkv, d) != (hkv2, d2) or v_new.shape != k_new.shape or v_pages.shape != k_pages.shape:
+        raise ValueError("k/v shapes disagree")
+    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
+        raise ValueError("page scales must be [num_blocks, Hkv]")
+    n = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != n or cu_seqlens_q.shape[0] != n + 1:
+        raise ValueError("block_table / cu_seqlens_q / context_lens sizes disagree")
+    args = [_dev(k_new, "k_new", torch.bfloat16, 3), _dev(v_new, "v_new", torch.bfloat16, 3),
+            _dev(k_pages, "k_pages", torch.uint8, 4), _dev(v_pages, "v_pages", torch.uint8, 4),
+            _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32), n, T, nb, hkv, d, bs,
+            _stream(stream)]
+    check(lib().reshape_and_cache_fp8(*args), "reshape_and_cache_fp8")
+
+
 def _attn_common(q, k_pages, v_pages, block_table, context_lens, out):
     torch = _torch()
     if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
@@ -217,6 +242,32 @@ def paged_attn_decode(q, k_pages, v_pages, block_table, context_lens, scale, tas
         _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
         [_dev(out, "out"), _stream(stream)]
     check(lib().paged_attn_decode(*args), "paged_attn_decode")
+
+
+def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, context_lens,
+                          scale, tasks_dev, combines_dev, num_partials, workspace, out,
+                          stream=None):
+    """Decode attention over fp8 pages with page scales (library kernels). q/out bf16
+    [N, Hq, D]; pages uint8 [NB, Hkv, bs, D]; scales float32 [NB, Hkv]."""
+    torch = _torch()
+    if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
+        raise ValueError("k_pages and v_pages must both be [NB, Hkv, bs, D]")
+    if q.dim() != 3 or out.shape != q.shape or q.shape[2] != k_pages.shape[3]:
+        raise ValueError("q and out must both be [N, Hq, D] with the pages' head_dim")
+    nb, hkv = k_pages.shape[:2]
+    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
+        raise ValueError("page scales must be [num_blocks, Hkv]")
+    n, hq, d = q.shape
+    if context_lens.shape[0] != n or block_table.dim() != 2 or block_table.shape[0] != n:
+        raise ValueError("decode takes one query row per sequence")
+    args = [_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
+            _dev(v_pages, "v_pages", torch.uint8), _dev(k_scales, "k_scales", torch.float32),
+            _dev(v_scales, "v_scales", torch.float32),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), n, hq, hkv, d, k_pages.shape[2],
+            float(scale)] + _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        [_dev(out, "out", torch.bfloat16), _stream(stream)]
+    check(lib().paged_attn_decode_fp8(*args), "paged_attn_decode_fp8")
 
 
 def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
@@ -271,9 +322,25 @@ class StepPlan:
         reshape_and_cache(k_new, v_new, k_pages, v_pages, self.block_table, self.cu, self.ctx,
                           stream)
 
+    def _check_decode_table(self, who):
+        if not self.decode_only or self.params.verify_rows:
+            raise ValueError(f"{who} runs decode tasks only: every q_len must be 1 and "
+                             "verify_rows 0 (use varlen for other batches)")
+
     def decode(self, q, k_pages, v_pages, scale, out, stream=None):
+        self._check_decode_table("decode")
         paged_attn_decode(q, k_pages, v_pages, self.block_table, self.ctx, scale, self.tasks,
                           self.combines, self.num_partials, self.workspace, out, stream)
+
+    def write_cache_fp8(self, k_new, v_new, k_pages, v_pages, k_scales, v_scales, stream=None):
+        reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, k_scales, v_scales,
+                              self.block_table, self.cu, self.ctx, stream)
+
+    def decode_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
+        self._check_decode_table("decode_fp8")
+        paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table,
+                              self.ctx, scale, self.tasks, self.combines, self.num_partials,
+                              self.workspace, out, stream)
 
     def varlen(self, q, k_pages, v_pages, scale, out, stream=None):
         paged_attn_varlen_prefill(q, k_pages, v_pages, self.block_table, self.cu, self.ctx,

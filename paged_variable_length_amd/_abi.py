@@ -24,7 +24,7 @@ PA_FP32 = 1
 PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -35,7 +35,8 @@ ERROR_NAMES = {
 # every symbol include/pagedattn.h declares
 EXPORTS = ("pa_abi_version", "pa_last_error", "pa_pack_seqlens", "build_task_table",
            "pa_workspace_bytes", "reshape_and_cache", "paged_attn_decode",
-           "paged_attn_varlen_prefill", "pa_validate_block_table")
+           "paged_attn_varlen_prefill", "pa_validate_block_table", "reshape_and_cache_fp8",
+           "paged_attn_decode_fp8")
 
 
 class PaTask(ctypes.Structure):
@@ -99,6 +100,13 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_varlen_prefill.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                             i32, ctypes.c_float, i32, p, i32, p, i32, i32, p,
                                             ctypes.c_size_t, p, p]
+    L.reshape_and_cache_fp8.restype = ctypes.c_int
+    L.reshape_and_cache_fp8.argtypes = [p, p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                                        i32, p]
+    L.paged_attn_decode_fp8.restype = ctypes.c_int
+    L.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, p, i32, p, i32, i32, p, ctypes.c_size_t,
+                                        p, p]
     L.pa_validate_block_table.restype = ctypes.c_int
     L.pa_validate_block_table.argtypes = [pi32, i32, pi32, i32, i32, i32]
     if L.pa_abi_version() != ABI_VERSION:

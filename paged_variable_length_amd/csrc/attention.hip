@@ -54,6 +54,8 @@ struct AttnArgs {
   float* ws_acc;                // [num_partials, D]
   float* ws_ml;                 // [num_partials, 2] (running max in log2 units, sum)
   void* out;
+  const float* k_scales;        // fp8 pages: [num_blocks, Hkv] scale per (block, kv head) page
+  const float* v_scales;
   int32_t max_blocks;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -68,6 +70,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Two E4M3FN codes (bytes 0,1 of w, or 2,3 with hi) times a page scale 2^k, as two bf16
+// values. The conversion applies the exponent of its scale operand; for a power of two that
+// is the exact product, and every E4M3FN value times 2^k (k >= -120) is a bf16 value (a
+// subnormal one at the bottom of the range), so nothing rounds.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -297,6 +308,216 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
     }
   }
   decode_merge_and_store<D>(a, t, tok, G, ncol, m, l, acc, smem, true);
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode body over fp8 pages: OCP E4M3FN codes with one power-of-two scale per (block, kv head)
+// page for K and one for V. Lane maps, softmax and outputs follow the bf16 body, except:
+//   QK: lane (i16, g4) loads 16 codes of key i16 at d = 64*j + 16*g4 (j < D/64); codes 0..7
+//       are its operand of k-step 2j, codes 8..15 of k-step 2j+1, and q is read in the same d
+//       order, so each dot product is the same sum;
+//   every code becomes bf16 with its page scale applied in the same exact conversion;
+//   a wave loads the raw codes of its next chunk before it computes the current one, and the
+//   block ids of the chunk after that, so a chunk of loads is always in flight per wave.
+// Decode tasks only (one query row per sequence).
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct Fp8VRaw;
+template <>
+struct Fp8VRaw<128> {
+  typedef u32x2 type;  // 8 codes along D
+};
+template <>
+struct Fp8VRaw<64> {
+  typedef uint32_t type;  // 4 codes along D
+};
+
+template <int D>
+struct Fp8Chunk {
+  u32x4 k[2][D / 64];               // [tile][j]: 16 codes of key i16 at d = 64*j + 16*g4
+  typename Fp8VRaw<D>::type v[8];   // slot e: key (tile e>>2, row 4*g4 + (e&3)), d = VEC*i16 + ..
+  float ksc[2], vsc[2];             // page scales of the two tiles
+};
+
+// dword w of a V slot (w < D/64): the whole slot for D = 64
+template <int D>
+__device__ __forceinline__ uint32_t vslot_word(const typename Fp8VRaw<D>::type& v, int w) {
+  if constexpr (D == 128)
+    return v[w];
+  else
+    return v;
+}
+
+template <int D>
+__device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem) {
+  constexpr int KS = D / 32;
+  constexpr int KJ = D / 64;
+  constexpr int VEC = D / 16;
+  typedef typename Fp8VRaw<D>::type VRaw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int s = t.seq, kvh = t.head;
+  const int tok = a.cu_seqlens ? a.cu_seqlens[s] : s;
+  const int bs = a.block_size;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<size_t>(tok) * a.num_q_heads + kvh * G + i16) * D + 16 * g4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (i16 < G) v = *reinterpret_cast<const u32x4*>(qp + 64 * (ks >> 1) + 8 * (ks & 1));
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+  const size_t head_stride = static_cast<size_t>(bs) * D;
+  const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pages) + kvh * head_stride;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pages) + kvh * head_stride;
+  const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_blocks;
+  const float c = a.scale_log2;
+  const int kv0 = t.kv0, kv1 = t.kv1;
+  const int nchunks = (kv1 - kv0 + 31) >> 5;
+
+  // block ids of chunk ch's two tiles; a tile at or past kv1 takes the block of key kv1 - 1,
+  // so its (weightless) loads stay inside the sequence's own pages
+  auto ids = [&](int ch, int (&blk)[2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) blk[tt] = bt[min(kv0 + 32 * ch + 16 * tt, kv1 - 1) >> a.bs_shift];
+  };
+  auto load = [&](int ch, const int (&blk)[2], Fp8Chunk<D>& r) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int ts = kv0 + 32 * ch + 16 * tt;
+      const size_t off =
+          static_cast<size_t>(blk[tt]) * block_stride + static_cast<size_t>(ts & (bs - 1)) * D;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j)
+        r.k[tt][j] = *reinterpret_cast<const u32x4*>(kbase + off + i16 * D + 64 * j + 16 * g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r.v[4 * tt + e] = *reinterpret_cast<const VRaw*>(vbase + off + (4 * g4 + e) * D + VEC * i16);
+      const size_t page = static_cast<size_t>(blk[tt]) * a.num_kv_heads + kvh;
+      r.ksc[tt] = a.k_scales[page];
+      r.vsc[tt] = a.v_scales[page];
+    }
+  };
+
+  f32x4 acc[VEC];
+#pragma unroll
+  for (int n = 0; n < VEC; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  auto compute = [&](int ch, const Fp8Chunk<D>& r) {
+    const int cs = kv0 + 32 * ch;
+    f32x4 sc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) {
+        const u32x4 w = r.k[tt][j];
+        const float ks = r.ksc[tt];
+        const u32x4 lo = {fp8x2_to_bf16x2<false>(w[0], ks), fp8x2_to_bf16x2<true>(w[0], ks),
+                          fp8x2_to_bf16x2<false>(w[1], ks), fp8x2_to_bf16x2<true>(w[1], ks)};
+        const u32x4 hi = {fp8x2_to_bf16x2<false>(w[2], ks), fp8x2_to_bf16x2<true>(w[2], ks),
+                          fp8x2_to_bf16x2<false>(w[3], ks), fp8x2_to_bf16x2<true>(w[3], ks)};
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), qf[2 * j], sc[tt], 0, 0, 0);
+        sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), qf[2 * j + 1], sc[tt], 0, 0, 0);
+      }
+    }
+    VRaw vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vr[e] = r.v[e];
+    if (cs + 32 > kv1) {
+      // tail chunk: keys past kv1 get no weight, and their codes become +0 so that
+      // 0 * value stays 0 in the value product
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = cs + 16 * (e >> 2) + 4 * g4 + (e & 3);
+        if (key >= kv1) {
+          sc[e >> 2][e & 3] = -INFINITY;
+          vr[e] = VRaw{};
+        }
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * c);
+    const float alpha = fast_exp2(m - mnew);
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], c, -mnew));
+      psum += p[e];
+    }
+    l = l * alpha + psum;
+    m = mnew;
+#pragma unroll
+    for (int n = 0; n < VEC; ++n) acc[n] *= alpha;
+    const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    const bf16x8 pf = as_bf16x8(pw);
+    // byte-interleaved slot pairs: pr[qd][w][h] holds value n = 4*w + 2*h + (0, 1) of slots
+    // 2*qd and 2*qd + 1 as bytes (slot 2qd, slot 2qd+1, slot 2qd, slot 2qd+1)
+    uint32_t pr[4][KJ][2];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+      for (int w = 0; w < KJ; ++w) {
+        const uint32_t ev = vslot_word<D>(vr[2 * qd], w), od = vslot_word<D>(vr[2 * qd + 1], w);
+        pr[qd][w][0] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+        pr[qd][w][1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+      }
+#pragma unroll
+    for (int n = 0; n < VEC; ++n) {
+      u32x4 vw;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        vw[qd] = (n & 1) ? fp8x2_to_bf16x2<true>(pr[qd][n >> 2][(n >> 1) & 1], r.vsc[qd >> 1])
+                         : fp8x2_to_bf16x2<false>(pr[qd][n >> 2][(n >> 1) & 1], r.vsc[qd >> 1]);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+    }
+  };
+
+  if (wave < nchunks) {
+    // two register buffers in turn (no copies, which would wait for the loads in flight)
+    int ch = wave;
+    int bn[2], bn2[2];
+    Fp8Chunk<D> ca, cb;
+    ids(ch, bn);
+    load(ch, bn, ca);
+    ids(ch + 4, bn);
+    while (true) {
+      if (ch + 4 >= nchunks) {
+        compute(ch, ca);
+        break;
+      }
+      ids(ch + 8, bn2);
+      load(ch + 4, bn, cb);
+      compute(ch, ca);
+      ch += 4;
+      bn[0] = bn2[0];
+      bn[1] = bn2[1];
+      if (ch + 4 >= nchunks) {
+        compute(ch, cb);
+        break;
+      }
+      ids(ch + 8, bn2);
+      load(ch + 4, bn, ca);
+      compute(ch, cb);
+      ch += 4;
+      bn[0] = bn2[0];
+      bn[1] = bn2[1];
+    }
+  }
+  decode_merge_and_store<D>(a, t, tok, G, G, m, l, acc, smem, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -919,6 +1140,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 }
 
 template <int D>
+__global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
+  __shared__ float smem[128 + 4 * 16 * D];
+  const pa_task t = a.tasks[blockIdx.x];
+  if (t.kind != PA_TASK_DECODE) return;
+  decode_task_fp8<D>(a, t, smem);
+}
+
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
@@ -998,6 +1227,111 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   }
 }
 
+// Cache write into fp8 pages (cann-recipes-infer page, section 5.2: values are scaled before
+// they are stored and each page keeps its scale). A page that this step writes into is
+// rescaled as a whole: its
+// valid rows -- the ones cached before (code * old scale, exact in fp32) and this step's rows
+// (bf16) -- set the page maximum, the new scale is the smallest power of two 2^k (k >= -120)
+// with max <= 448 * 2^k, and every valid row is encoded again as the round-to-nearest-even
+// E4M3FN code of value * 2^-k (an exact scaling). Rows past the context stay untouched.
+// Grid: x = packed token, y = groups of four (tensor, kv head) units, one wave per unit. Only
+// the token that is the first new row of its block does work, so each touched page is
+// rewritten by exactly one wave. Two passes over the page: the maximum, then the codes; each
+// lane reads and writes the same eight codes in both, and the new codes and scale depend on
+// the maximum over all lanes' reads, so no write precedes a read of the old page.
+template <int D>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
+    const __bf16* k_new, const __bf16* v_new, uint8_t* k_pages, uint8_t* v_pages,
+    float* k_scales, float* v_scales, const int32_t* block_table, int32_t max_blocks,
+    const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_kv_heads, int32_t block_size, int32_t bs_shift) {
+  const int unit = blockIdx.y * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= 2 * num_kv_heads) return;
+  const int t = blockIdx.x;
+  int lo_s = 0, hi_s = num_seqs;  // cu[lo_s] <= t < cu[hi_s]
+  while (hi_s - lo_s > 1) {
+    const int mid = (lo_s + hi_s) >> 1;
+    if (cu_seqlens[mid] <= t) lo_s = mid; else hi_s = mid;
+  }
+  const int s = lo_s;
+  const int qlen = cu_seqlens[s + 1] - cu_seqlens[s];
+  const int ctx = context_lens[s];
+  const int P = ctx - qlen;
+  const int pos = P + (t - cu_seqlens[s]);
+  if (pos != P && (pos & (block_size - 1)) != 0) return;  // not the first new row of its block
+  const int lb = pos >> bs_shift;
+  const int row0 = lb << bs_shift;                          // position of the block's slot 0
+  const int n_valid = min(ctx, row0 + block_size) - row0;
+  const int n_old = pos - row0;                             // rows cached before this step
+  const int blk = block_table[static_cast<size_t>(s) * max_blocks + lb];
+  const int lane = threadIdx.x & 63;
+  const int which = unit >= num_kv_heads;                   // 0: K, 1: V
+  const int g = unit - which * num_kv_heads;
+  uint8_t* codes = (which ? v_pages : k_pages) +
+                   (static_cast<size_t>(blk) * num_kv_heads + g) * block_size * D;
+  float* scale_p = (which ? v_scales : k_scales) + static_cast<size_t>(blk) * num_kv_heads + g;
+  const __bf16* src = (which ? v_new : k_new) + g * D;
+  const int64_t tok_p = static_cast<int64_t>(cu_seqlens[s]) - P;  // packed token of position 0
+  const float old_scale = n_old > 0 ? *scale_p : 1.f;
+  constexpr int Q8 = D / 8;                                 // eight-code groups per row
+  const int groups = n_valid * Q8;
+  // values of group e (row e / Q8, d = 8 * (e % Q8) + 0..7)
+  auto load8 = [&](int e, float (&x)[8]) {
+    const int j = e / Q8, q = e - j * Q8;
+    if (j < n_old) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(codes + j * D + 8 * q);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int c = static_cast<int>(w[h >> 1]);
+        const f32x2 v = (h & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(c, true)
+                                : __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+        x[2 * h] = v[0] * old_scale;
+        x[2 * h + 1] = v[1] * old_scale;
+      }
+    } else {
+      // position row0 + j is a new row: packed token cu[s] + (row0 + j - P)
+      const u32x4 w = *reinterpret_cast<const u32x4*>(
+          src + static_cast<size_t>(tok_p + row0 + j) * num_kv_heads * D + 8 * q);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[2 * h] = __builtin_bit_cast(float, w[h] << 16);
+        x[2 * h + 1] = __builtin_bit_cast(float, w[h] & 0xffff0000u);
+      }
+    }
+  };
+  float amax = 0.f;
+  for (int e = lane; e < groups; e += 64) {
+    float x[8];
+    load8(e, x);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(x[u]));
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) amax = fmaxf(amax, wave_shfl_xor(amax, sh));
+  int k = 0;
+  if (amax > 0.f) {
+    const int e2 = ilogbf(amax);                            // 2^e2 <= amax < 2^(e2+1)
+    k = amax <= ldexpf(1.75f, e2) ? e2 - 8 : e2 - 7;        // 448 * 2^(e2-8) = 1.75 * 2^e2
+    k = max(k, -120);
+  }
+  for (int e = lane; e < groups; e += 64) {
+    float x[8];
+    load8(e, x);
+    u32x2 w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h], -k), ldexpf(x[4 * h + 1], -k), 0,
+                                              false);
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * h + 2], -k), ldexpf(x[4 * h + 3], -k), c,
+                                          true);
+      w[h] = static_cast<uint32_t>(c);
+    }
+    const int j = e / Q8, q = e - j * Q8;
+    *reinterpret_cast<u32x2*>(codes + j * D + 8 * q) = w;
+  }
+  if (lane == 0) *scale_p = ldexpf(1.f, k);
+}
+
 int log2i(int x) {
   int r = 0;
   while ((1 << r) < x) ++r;
@@ -1048,6 +1382,8 @@ AttnArgs make_args(const void* q, const void* kp, const void* vp, const int32_t*
   size_t acc_bytes = (static_cast<size_t>(num_partials) * d * sizeof(float) + 255) & ~size_t(255);
   a.ws_ml = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + acc_bytes) : nullptr;
   a.out = out;
+  a.k_scales = nullptr;
+  a.v_scales = nullptr;
   a.max_blocks = max_blocks;
   a.num_q_heads = hq;
   a.num_kv_heads = hkv;
@@ -1180,4 +1516,75 @@ extern "C" int paged_attn_varlen_prefill(
     launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
   }
   return hip_check("paged_attn_varlen_prefill");
+}
+
+extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages,
+                                     void* v_pages, float* k_scales, float* v_scales,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t num_blocks,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: negative size");
+  if (num_kv_heads < 1 || !pa::head_dim_ok(head_dim))
+    return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: Hkv %d, head_dim %d", num_kv_heads,
+                         head_dim);
+  if (!pa::block_size_ok(block_size))
+    return pa::set_error(PA_ERR_BLOCK_SIZE, "reshape_and_cache_fp8: block_size %d", block_size);
+  if (num_tokens == 0) return pa::clear_error();
+  if (!k_new || !v_new || !k_pages || !v_pages || !k_scales || !v_scales || !block_table ||
+      !cu_seqlens_q || !context_lens)
+    return pa::set_error(PA_ERR_NULL, "reshape_and_cache_fp8: NULL pointer");
+  if (num_seqs < 1)
+    return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: tokens without sequences");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int shift = log2i(block_size);
+  const unsigned units = (2 * num_kv_heads + kThreads / 64 - 1) / (kThreads / 64);
+#define PA_RC8_LAUNCH(DD)                                                                      \
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DD>, dim3(num_tokens, units), dim3(kThreads), 0, st, \
+                     static_cast<const __bf16*>(k_new), static_cast<const __bf16*>(v_new),      \
+                     static_cast<uint8_t*>(k_pages), static_cast<uint8_t*>(v_pages), k_scales,  \
+                     v_scales, block_table, max_blocks_per_seq, cu_seqlens_q, context_lens,     \
+                     num_seqs, num_kv_heads, block_size, shift)
+  if (head_dim == 128)
+    PA_RC8_LAUNCH(128);
+  else
+    PA_RC8_LAUNCH(64);
+#undef PA_RC8_LAUNCH
+  return hip_check("reshape_and_cache_fp8");
+}
+
+extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, float scale,
+                                     const pa_task* tasks_dev, int32_t num_tasks,
+                                     const pa_combine* combines_dev, int32_t num_combines,
+                                     int32_t num_partials, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream) {
+  if (int rc = check_attn_scalars("paged_attn_decode_fp8", num_seqs, num_q_heads, num_kv_heads,
+                                  head_dim, block_size, PA_BF16, num_tasks, num_combines,
+                                  num_partials, workspace_bytes, workspace, max_blocks_per_seq))
+    return rc;
+  if (num_tasks == 0) return pa::clear_error();
+  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !out ||
+      !tasks_dev || (num_combines > 0 && !combines_dev))
+    return pa::set_error(PA_ERR_NULL, "paged_attn_decode_fp8: NULL pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, nullptr,
+                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                         tasks_dev, num_tasks, num_partials, workspace, out);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(decode_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    launch_combine<__bf16, 128>(combines_dev, num_combines, nullptr, a, st);
+  } else {
+    hipLaunchKernelGGL(decode_fp8_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    launch_combine<__bf16, 64>(combines_dev, num_combines, nullptr, a, st);
+  }
+  return hip_check("paged_attn_decode_fp8");
 }

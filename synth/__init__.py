@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_workload", "deal_block_table", "make_values",
-           "custom_workload"]
+           "make_fp8_pages", "custom_workload"]
 
 
 @dataclass
@@ -103,6 +103,10 @@ def _lengths(name: str, rng: np.random.Generator):
         q = np.concatenate([np.ones(200, np.int64), np.full(4, 512, np.int64)])
         ctx = np.concatenate([dec_ctx, prefix + 512])
         return q, ctx, 64, 8, 128, 128, "bf16", None
+    if name == "decode_mha_fp8":
+        # the MHA decode batch (same lengths) over fp8 pages with per-page scales
+        ctx = rng.integers(128, 4097, size=64).astype(np.int64)
+        return np.ones(64, np.int64), ctx, 32, 32, 128, 16, "bf16", None
     if name == "verify_gqa_bf16":
         # the GQA decode batch with a 4-row draft per sequence (3 drafted tokens plus the last
         # accepted one) verified in one step; contexts include the draft rows
@@ -121,6 +125,7 @@ WORKLOADS = {
     "prefill_varlen_bf16": 4,
     "mixed_bf16": 5,
     "verify_gqa_bf16": 6,
+    "decode_mha_fp8": 2,
 }
 
 
@@ -190,3 +195,48 @@ def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinel
         k_pages.transpose(1, 2)[mask] = float("nan")
         v_pages.transpose(1, 2)[mask] = float("nan")
     return dict(q=q, k_new=k_new, v_new=v_new, k_pages=k_pages, v_pages=v_pages)
+
+
+def make_fp8_pages(w: Workload, device="cpu", seed: int | None = None, nan_sentinels=True):
+    """Draw an fp8 page pool for a workload: uint8 codes [NB, Hkv, bs, D] and float32 page
+    scales [NB, Hkv].
+
+    Codes are uniform over the finite OCP E4M3FN codes (0x00..0x7E with a random sign bit), so
+    every magnitude of the format occurs; scales are 2^-e with e uniform in {6, 7, 8} per page.
+    Nothing here encodes values: the codes are drawn directly. With ``nan_sentinels`` every slot
+    that holds no cached key (as in make_values) holds the NaN code 0x7F, and the scales of
+    blocks no sequence owns are NaN.
+    """
+    import torch
+    seed = (w.seed if seed is None else seed) + 7919
+    rng = np.random.default_rng(seed)
+    hkv, d, bs, nb = w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks
+
+    def codes():
+        mag = rng.integers(0, 0x7F, size=(nb, hkv, bs, d), dtype=np.uint8)
+        sign = (rng.integers(0, 2, size=(nb, hkv, bs, d), dtype=np.uint8) << 7).astype(np.uint8)
+        return mag | sign
+
+    k_codes, v_codes = codes(), codes()
+    k_scales = np.exp2(-rng.integers(6, 9, size=(nb, hkv))).astype(np.float32)
+    v_scales = np.exp2(-rng.integers(6, 9, size=(nb, hkv))).astype(np.float32)
+    if nan_sentinels:
+        valid = np.zeros((nb, bs), dtype=bool)
+        owned = np.zeros(nb, dtype=bool)
+        for s in range(w.num_seqs):
+            prefix = int(w.ctx_lens[s] - w.q_lens[s])
+            nblk = (int(w.ctx_lens[s]) + bs - 1) // bs
+            for j in range(nblk):
+                b = int(w.block_table[s, j])
+                owned[b] = True
+                lo, hi = j * bs, min((j + 1) * bs, prefix)
+                if hi > lo:
+                    valid[b, : hi - lo] = True
+        k_codes.transpose(0, 2, 1, 3)[~valid] = 0x7F
+        v_codes.transpose(0, 2, 1, 3)[~valid] = 0x7F
+        k_scales[~owned] = np.nan
+        v_scales[~owned] = np.nan
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
+         for k, v in dict(k_codes=k_codes, v_codes=v_codes, k_scales=k_scales,
+                          v_scales=v_scales).items()}
+    return t

@@ -215,3 +215,17 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pa.reshape_and_cache(k, k, pages, pages, i, torch.zeros(3, dtype=torch.int32),
                              torch.zeros(2, dtype=torch.int32))
+
+
+def test_step_plan_decode_refuses_non_decode_tables():
+    """The decode entry points run decode tasks only: a plan with a multi-row sequence or with
+    verify rows must go through varlen instead (checked before any device call)."""
+    import torch
+    table = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    q = torch.zeros(1)
+    for q_lens, extra in (([2, 1], {}), ([1, 1], {"verify_rows": 2})):
+        plan = pa.StepPlan(q_lens, [20, 17], table, 8, 2, 128, 16, device="cpu", **extra)
+        with pytest.raises(ValueError, match="decode tasks only"):
+            plan.decode(q, q, q, 0.1, q)
+        with pytest.raises(ValueError, match="decode tasks only"):
+            plan.decode_fp8(q, q, q, q, q, 0.1, q)
