@@ -28,11 +28,38 @@ Readings taken where the pages leave the step open:
   * the page's own code deals sorted tasks with i % num_cores while its prose says
     "symmetric round robin"; both balance ratios are reported.
 
+Shared prefixes (XY-Serve page, "自动前缀缓存": requests that repeat a prompt prefix reuse its
+cached keys and values; ATB page, "KV缓存复用": a later turn reuses the blocks of the earlier
+ones). When the block table makes several sequences point at the same physical blocks, the
+attention over those keys can read them once for all of them. Readings:
+  * sharing is looked for between neighbouring decode sequences (q_len 1) in batch order, and
+    only when ``shared_min`` > 0 and a task's 16 columns hold at least two sequences
+    (G <= 8); the host has a copy of the block table;
+  * two neighbours share the leading logical blocks whose physical ids are equal (among the
+    blocks both need); a block that receives either one's new row this step must not be
+    shared (an input error); their shared keys are those blocks' keys, rounded down to a
+    multiple of 64;
+  * a group is a maximal run of neighbours that share at least ``shared_min`` keys pairwise;
+    the group's shared length L is the smallest pairwise value (equal ids are transitive);
+  * a group is cut into ceil(n / (16 // G)) column sets of consecutive members with sizes as
+    equal as possible (the first n % sets one larger);
+  * per kv head and column set: [0, L) in pieces of ``dec_split`` as shared tasks whose
+    columns are (member, query head) pairs, and each member's own keys [L, ctx) in pieces of
+    ``dec_split`` as decode tasks; every member's row merges all its pieces, so each member
+    gets partial rows and one combine record even with a single piece;
+  * partial rows of a column set: member i owns W = (S + max U) * G rows from base + i*W
+    (S shared pieces, U_i own pieces), piece k's rows at + k*G; a shared task's partial field
+    is base + k*G and its q_row0 field holds the member stride W; rows past S + U_i of a
+    member with fewer own pieces stay unused;
+  * a shared task's load is keys x members x G (pairs x heads, as for every task).
+
 Records (8 int32 each):
   task    = (kind, seq, head, q_row0, q_rows, kv0, kv1, partial)
             kind 0 = decode split, head = kv head (covers query heads head*G .. head*G+G-1)
             kind 1 = prefill tile, head = query head
             kind 2 = verify split, head = kv head, q_rows = the sequence's rows, q_row0 = 0
+            kind 3 = shared-prefix split, seq = first member, q_rows = members (consecutive
+                     decode sequences), q_row0 = member stride W of its partial rows
   combine = (seq, q_row0, q_rows, head, heads, first_slot, n_slots, 0)
             partial row of split k, query row i, head j = first_slot + k*q_rows*heads + i*heads + j
 """
@@ -65,6 +92,7 @@ class Params:
     num_workers: int = 256
     decode_weight: int = 1
     verify_rows: int = 0
+    shared_min: int = 0
 
 
 def _check(p: Params, cu, ctx):
@@ -84,6 +112,8 @@ def _check(p: Params, cu, ctx):
         raise TaskTableError(ERR_SHAPE, "num_workers and decode_weight must be >= 1")
     if p.verify_rows != 0 and not 2 <= p.verify_rows <= 16:
         raise TaskTableError(ERR_SHAPE, "verify_rows must be 0 or lie in [2, 16]")
+    if p.shared_min < 0 or p.shared_min % 64:
+        raise TaskTableError(ERR_SHAPE, "shared_min must be 0 or a positive multiple of 64")
     # cann-recipes-infer page, section 4.4: offsets start at 0 and increase strictly
     if len(cu) != len(ctx) + 1 or cu[0] != 0:
         raise TaskTableError(ERR_INPUT, "cu_seqlens must have N+1 entries starting at 0")
@@ -98,9 +128,30 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def build_task_table(p: Params, cu_seqlens_q, context_lens):
+def shared_keys_with_previous(p: Params, cu, ctx, block_table):
+    """pair[s] for s >= 1: keys that decode sequences s-1 and s both read from the same physical
+    blocks, rounded down to a multiple of 64 (0 when either is not a decode row)."""
+    bs = p.block_size
+    pair = [0] * len(ctx)
+    for s in range(1, len(ctx)):
+        if cu[s + 1] - cu[s] != 1 or cu[s] - cu[s - 1] != 1:
+            continue
+        need = min(_ceil_div(ctx[s - 1], bs), _ceil_div(ctx[s], bs))
+        common = 0
+        while common < need and int(block_table[s - 1][common]) == int(block_table[s][common]):
+            common += 1
+        # logical block (ctx-1)//bs receives the sequence's new row in this step
+        if common > min((ctx[s - 1] - 1) // bs, (ctx[s] - 1) // bs):
+            raise TaskTableError(ERR_INPUT, f"sequences {s - 1} and {s} share a block that "
+                                 "receives a new row")
+        pair[s] = common * bs // 64 * 64
+    return pair
+
+
+def build_task_table(p: Params, cu_seqlens_q, context_lens, block_table=None):
     """Return (tasks int32 [n, 8], combines int32 [m, 8], num_partials, loads int64 [n],
-    balance dict {"snake", "modulo"})."""
+    balance dict {"snake", "modulo"}). ``block_table`` (host, [N, max_blocks]) is needed only
+    when ``p.shared_min`` > 0."""
     cu = [int(x) for x in cu_seqlens_q]
     ctx = [int(x) for x in context_lens]
     _check(p, cu, ctx)
@@ -108,7 +159,54 @@ def build_task_table(p: Params, cu_seqlens_q, context_lens):
     emitted = []          # (load, task) in emission order
     combines = []
     num_partials = 0
-    for s in range(len(ctx)):
+    columns = 16 // G     # sequences per shared task
+    pair = [0] * len(ctx)
+    if p.shared_min > 0:
+        if block_table is None:
+            raise TaskTableError(ERR_INPUT, "shared_min > 0 needs the block table")
+        for s in range(len(ctx)):
+            if _ceil_div(ctx[s], p.block_size) > len(block_table[s]):
+                raise TaskTableError(ERR_SHAPE, "block table narrower than a context needs")
+        pair = shared_keys_with_previous(p, cu, ctx, block_table)
+    ds, w = p.dec_split, p.decode_weight
+    s = 0
+    while s < len(ctx):
+        end = s
+        if p.shared_min > 0 and columns >= 2:
+            while end + 1 < len(ctx) and pair[end + 1] >= p.shared_min:
+                end += 1
+        if end > s:
+            # a shared-prefix group: members s .. end
+            L = min(pair[s + 1:end + 1])
+            n = end - s + 1
+            nsets = _ceil_div(n, columns)
+            sizes = [n // nsets + (1 if i < n % nsets else 0) for i in range(nsets)]
+            S = _ceil_div(L, ds)
+            for g in range(p.num_kv_heads):
+                m0 = s
+                for size in sizes:
+                    members = list(range(m0, m0 + size))
+                    U = [_ceil_div(ctx[m] - L, ds) for m in members]
+                    W = (S + max(U)) * G
+                    base = num_partials
+                    num_partials += size * W
+                    for i, m in enumerate(members):
+                        combines.append((m, 0, 1, g * G, G, base + i * W, S + U[i], 0))
+                    for k in range(S):
+                        kv0 = k * ds
+                        kv1 = min(L, kv0 + ds)
+                        emitted.append(((kv1 - kv0) * size * G * w,
+                                        (3, m0, g, W, size, kv0, kv1, base + k * G)))
+                    for i, m in enumerate(members):
+                        for j in range(U[i]):
+                            kv0 = L + j * ds
+                            kv1 = min(ctx[m], kv0 + ds)
+                            emitted.append(((kv1 - kv0) * G * w,
+                                            (0, m, g, 0, 1, kv0, kv1,
+                                             base + i * W + (S + j) * G)))
+                    m0 += size
+            s = end + 1
+            continue
         ql = cu[s + 1] - cu[s]
         prefix = ctx[s] - ql
         verify = 2 <= ql <= p.verify_rows and G * ql <= 16
@@ -150,6 +248,7 @@ def build_task_table(p: Params, cu_seqlens_q, context_lens):
                             load += max(0, min(kv1, prefix + i + 1) - kv0)
                         part = first + k * rows if nsplit > 1 else -1
                         emitted.append((load, (1, s, h, r0, rows, kv0, kv1, part)))
+        s += 1
     # stable sort, load descending (ties keep emission order)
     order = sorted(range(len(emitted)), key=lambda i: -emitted[i][0])
     tasks = np.array([emitted[i][1] for i in order], dtype=np.int32).reshape(-1, 8)

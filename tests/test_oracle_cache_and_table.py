@@ -144,11 +144,14 @@ def coverage(p, cu, ctx, tasks):
     G = p.num_q_heads // p.num_kv_heads
     cnt = {}
     for kind, s, head, r0, rows, kv0, kv1, _ in tasks.tolist():
-        heads = range(head * G, head * G + G) if kind in (0, 2) else [head]
-        P_ = ctx[s] - (cu[s + 1] - cu[s])
-        for h, i in itertools.product(heads, range(r0, r0 + rows)):
+        heads = range(head * G, head * G + G) if kind in (0, 2, 3) else [head]
+        # a shared-prefix task covers row 0 of `rows` consecutive sequences
+        cells = [(s + i, 0) for i in range(rows)] if kind == 3 else \
+            [(s, i) for i in range(r0, r0 + rows)]
+        for h, (sq, i) in itertools.product(heads, cells):
+            P_ = ctx[sq] - (cu[sq + 1] - cu[sq])
             for j in range(kv0, min(kv1, P_ + i + 1)):
-                cnt[(s, h, i, j)] = cnt.get((s, h, i, j), 0) + 1
+                cnt[(sq, h, i, j)] = cnt.get((sq, h, i, j), 0) + 1
     return cnt
 
 
@@ -204,3 +207,168 @@ def test_validation_codes():
 def test_empty_batch():
     tasks, comb, npart, loads, bal = ot.build_task_table(P(), [0], [])
     assert tasks.shape == (0, 8) and comb.shape == (0, 8) and npart == 0
+
+
+# ---- shared prefixes (blocks aliased between neighbouring decode sequences) ----
+
+def test_hand_derived_shared_table():
+    """Three decode sequences, ctx 100, 90, 120, bs 16, Hq=2, Hkv=1 (G=2, 8 sequences per
+    shared task), dec_split 64, shared_min 64. Block rows:
+      s0: 0 1 2 3 4 5 6      s1: 0 1 2 3 4 7 8      s2: 0 1 2 3 9 10 11 12
+    s0/s1 share 5 blocks (80 keys -> 64), s1/s2 share 4 (64): one group, L = 64, one column
+    set of 3 members. S = 1 shared piece [0, 64); own pieces [64, 100), [64, 90), [64, 120)
+    (U = 1 each); W = (1 + 1) * 2 = 4, base 0: member i owns rows 4i .. 4i+3.
+    Emission: combines s0, s1, s2; shared task (load 64*3*2 = 384); s0 (36*2 = 72),
+    s1 (26*2 = 52), s2 (56*2 = 112). Sorted: 384, 112, 72, 52."""
+    bt = np.array([[0, 1, 2, 3, 4, 5, 6, -1], [0, 1, 2, 3, 4, 7, 8, -1],
+                   [0, 1, 2, 3, 9, 10, 11, 12]])
+    p = P(shared_min=64)
+    tasks, comb, npart, loads, _ = ot.build_task_table(p, [0, 1, 2, 3], [100, 90, 120], bt)
+    assert tasks.tolist() == [
+        [3, 0, 0, 4, 3, 0, 64, 0],
+        [0, 2, 0, 0, 1, 64, 120, 10],
+        [0, 0, 0, 0, 1, 64, 100, 2],
+        [0, 1, 0, 0, 1, 64, 90, 6]]
+    assert loads.tolist() == [384, 112, 72, 52]
+    assert comb.tolist() == [[0, 0, 1, 0, 2, 0, 2, 0], [1, 0, 1, 0, 2, 4, 2, 0],
+                             [2, 0, 1, 0, 2, 8, 2, 0]]
+    assert npart == 12
+    # sharing off: the plain table, whatever the block table holds
+    plain = ot.build_task_table(P(), [0, 1, 2, 3], [100, 90, 120])
+    off = ot.build_task_table(P(), [0, 1, 2, 3], [100, 90, 120], bt)
+    assert np.array_equal(plain[0], off[0]) and np.array_equal(plain[1], off[1])
+
+
+def test_shared_rules():
+    bt = np.array([[0, 1, 2, 3, 4, 5, 6, -1], [0, 1, 2, 3, 4, 7, 8, -1]])
+    # below shared_min: no group
+    tasks, *_ = ot.build_task_table(P(shared_min=128), [0, 1, 2], [100, 90], bt)
+    assert 3 not in tasks[:, 0]
+    # a prefill neighbour breaks the run
+    tasks, *_ = ot.build_task_table(P(shared_min=64), [0, 1, 3], [100, 90], bt)
+    assert 3 not in tasks[:, 0]
+    # G = 16: one sequence per 16 columns, no sharing
+    tasks, *_ = ot.build_task_table(P(num_q_heads=16, shared_min=64), [0, 1, 2], [100, 90], bt)
+    assert 3 not in tasks[:, 0]
+    # a shared block that receives a new row is an input error
+    bad = np.array([[0, 1, 2], [0, 1, 5]])
+    tasks, *_ = ot.build_task_table(P(shared_min=32 * 2), [0, 1, 2], [40, 48], bad)
+    assert 3 not in tasks[:, 0]                   # each writes its own block 2; 32 keys shared
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(shared_min=64), [0, 1, 2], [40, 48], np.array([[0, 1, 2]] * 2))
+    assert e.value.code == ot.ERR_INPUT           # both write physical block 2
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(shared_min=64), [0, 1, 2], [32, 48], bad)   # s0 writes block 1
+    assert e.value.code == ot.ERR_INPUT
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(shared_min=64), [0, 1, 2], [100, 90])       # no block table
+    assert e.value.code == ot.ERR_INPUT
+    with pytest.raises(ot.TaskTableError) as e:
+        ot.build_task_table(P(shared_min=32), [0, 1, 2], [100, 90], bt)
+    assert e.value.code == ot.ERR_SHAPE
+
+
+def test_shared_column_sets_are_balanced():
+    """G = 4 gives 4 sequences per shared task: a group of 9 becomes sets of 3, 3, 3 and a
+    group of 6 sets of 3 and 3."""
+    for n, sizes in ((9, [3, 3, 3]), (6, [3, 3]), (4, [4]), (5, [3, 2])):
+        bt = np.array([[0, 1, 2, 3, 100 + s] for s in range(n)])
+        p = P(num_q_heads=4, shared_min=64)
+        tasks, *_ = ot.build_task_table(p, list(range(n + 1)), [70] * n, bt)
+        got = sorted(((t[1], t[4]) for t in tasks.tolist() if t[0] == 3))
+        assert [r for _, r in got] == sizes
+        assert [f for f, _ in got] == list(np.cumsum([0] + sizes[:-1]))
+
+
+def _aliased_batch(rng, bs, n_groups, G):
+    """Decode sequences in runs that share a random number of leading blocks, a prefill and a
+    verify sequence in between, and private blocks for everything else."""
+    rows, ctx, q = [], [], []
+    nxt = 1000
+    for g in range(n_groups):
+        shared = [nxt + i for i in range(int(rng.integers(0, 17)))]
+        nxt += len(shared)
+        for m in range(int(rng.integers(1, 6))):
+            c = len(shared) * bs + int(rng.integers(1, 200))
+            need = -(-c // bs)
+            row = shared + list(range(nxt, nxt + need - len(shared)))
+            nxt += need - len(shared)
+            rows.append(row)
+            ctx.append(c)
+            q.append(1)
+        if g % 2:
+            c = int(rng.integers(5, 90))
+            rows.append(list(range(nxt, nxt + -(-c // bs))))
+            nxt += -(-c // bs)
+            ctx.append(c)
+            q.append(int(rng.integers(2, 5)))
+    width = max(len(r) for r in rows)
+    bt = np.full((len(rows), width), -1, dtype=np.int64)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    return q, ctx, bt
+
+
+@pytest.mark.parametrize("seed,G,bs,dec_split,shared_min",
+                         [(1, 1, 16, 64, 64), (2, 2, 16, 128, 64), (3, 4, 32, 64, 128),
+                          (4, 8, 64, 64, 64), (5, 1, 16, 64, 192)])
+def test_shared_coverage_and_partials(seed, G, bs, dec_split, shared_min):
+    rng = np.random.default_rng(seed)
+    q_lens, ctx, bt = _aliased_batch(rng, bs, 8, G)
+    cu = oa.pack_lengths(q_lens).tolist()
+    hkv = 2
+    p = P(num_q_heads=hkv * G, num_kv_heads=hkv, block_size=bs, dec_split=dec_split,
+          pf_q_tile=3, verify_rows=4, shared_min=shared_min, num_workers=5)
+    _check_shared_table(p, cu, ctx, bt, q_lens, G)
+
+
+def _check_shared_table(p, cu, ctx, bt, q_lens, G):
+    bs, hkv = p.block_size, p.num_kv_heads
+    tasks, comb, npart, loads, _ = ot.build_task_table(p, cu, ctx, bt)
+    assert 3 in tasks[:, 0]
+    cnt = coverage(p, cu, ctx, tasks)
+    hq = hkv * G
+    expect = {(s, h, i, j) for s in range(len(q_lens)) for h in range(hq)
+              for i in range(q_lens[s]) for j in range(ctx[s] - q_lens[s] + i + 1)}
+    assert set(cnt) == expect and all(v == 1 for v in cnt.values())
+    # loads: pairs x heads, whatever task covers them
+    assert int(loads.sum()) == len(expect)
+    # shared tasks: members are consecutive decode sequences that really alias [0, kv1)
+    for kind, s, head, W, rows, kv0, kv1, part in tasks.tolist():
+        if kind == 3:
+            for m in range(s, s + rows):
+                assert q_lens[m] == 1 and kv1 <= ctx[m] - 1
+                nb = -(-kv1 // bs)
+                assert np.array_equal(bt[m, :nb], bt[s, :nb])
+    # partial rows: written once each; every combine slot reads exactly the written rows
+    written = []
+    for kind, s, head, W, rows, kv0, kv1, part in tasks.tolist():
+        if part < 0:
+            continue
+        if kind == 3:
+            written += [part + i * W + j for i in range(rows) for j in range(G)]
+        elif kind in (0, 2):
+            written += list(range(part, part + rows * G))
+        else:
+            written += list(range(part, part + rows))
+    assert len(written) == len(set(written)) and max(written) < npart
+    read = []
+    for sq, r0, rows, head, heads, first, n, _ in comb.tolist():
+        read += [first + k * rows * heads + i for k in range(n) for i in range(rows * heads)]
+    assert sorted(read) == sorted(written)
+
+
+def test_planted_shared_length_mistake_is_caught(monkeypatch):
+    """An oracle whose pairwise shared length runs one 64-key step past the aliased blocks
+    must fail the aliasing pin."""
+    rng = np.random.default_rng(1)
+    q_lens, ctx, bt = _aliased_batch(rng, 16, 8, 1)
+    cu = oa.pack_lengths(q_lens).tolist()
+    p = P(num_q_heads=2, num_kv_heads=2, block_size=16, dec_split=64, pf_q_tile=3,
+          verify_rows=4, shared_min=64, num_workers=5)
+    _check_shared_table(p, cu, ctx, bt, q_lens, 1)
+    real = ot.shared_keys_with_previous
+    monkeypatch.setattr(ot, "shared_keys_with_previous",
+                        lambda *a: [v + 64 if v > 0 else v for v in real(*a)])
+    with pytest.raises(AssertionError):
+        _check_shared_table(p, cu, ctx, bt, q_lens, 1)
