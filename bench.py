@@ -36,7 +36,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
-             "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8"]
+             "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8",
+             "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing"]
 # Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
 # splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
 # query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
@@ -52,6 +53,10 @@ TILING = {
     "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
     # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline)
     "decode_mha_fp8": dict(dec_split=1024),
+    # 8 prompts x 16 decoding requests that alias the prompt's blocks: the prefix is read once
+    # per group and kv head; the variant runs the same batch without grouping
+    "decode_shared_mha_bf16": dict(dec_split=1024, shared_min=64),
+    "decode_shared_mha_bf16:no_sharing": dict(dec_split=1024),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
@@ -84,23 +89,35 @@ def algorithmic_work(w, fp8_pages=False):
     """Bytes the method must move and flops it must do, counting valid data only: every
     visible K/V row once (one byte per element for fp8 pages, plus the K and V scale of each
     (block, kv head) page read), q and out once, the block-table entries a sequence needs, its
-    length; flops = 4*D per unmasked (query row, key) pair per query head."""
+    length; flops = 4*D per unmasked (query row, key) pair per query head. A K/V row that
+    several sequences alias (a shared prefix) is one row of HBM data: the bytes count distinct
+    cached (block, slot) pairs, which equals the sum of the contexts when nothing is aliased."""
     esize = 2 if w.dtype == "bf16" else 4
     kv_size = 1 if fp8_pages else esize
     e_kv = 2 * w.num_kv_heads * w.head_dim * kv_size
     ctx = w.ctx_lens.astype(np.int64)
+    # a slot is counted once if any sequence reads it; a sequence's last block holds only its
+    # first ctx - (nblk - 1) * bs slots
+    used = np.zeros((w.num_blocks, w.block_size), dtype=bool)
+    for s_ in range(w.num_seqs):
+        c = int(ctx[s_])
+        nb_ = (c + w.block_size - 1) // w.block_size
+        used[w.block_table[s_, :nb_ - 1]] = True
+        used[w.block_table[s_, nb_ - 1], :c - (nb_ - 1) * w.block_size] = True
+    distinct = int(used.sum())
     q = w.q_lens.astype(np.int64)
     nblk = (ctx + w.block_size - 1) // w.block_size
     T = int(q.sum())
     scale_bytes = int(nblk.sum()) * w.num_kv_heads * 2 * 4 if fp8_pages else 0
-    B = int(ctx.sum()) * e_kv + T * w.num_q_heads * w.head_dim * esize * 2 + int(nblk.sum()) * 4 \
+    B = distinct * e_kv + T * w.num_q_heads * w.head_dim * esize * 2 + int(nblk.sum()) * 4 \
         + 4 * w.num_seqs + scale_bytes
     P = ctx - q
     pairs = P * q + q * (q + 1) // 2                      # sum over rows i of (P + i + 1)
     dec = q == 1
     F_dec = int((pairs[dec]).sum()) * w.num_q_heads * 4 * w.head_dim
     F_pre = int((pairs[~dec]).sum()) * w.num_q_heads * 4 * w.head_dim
-    B_dec = int(ctx[dec].sum()) * e_kv + int(dec.sum()) * w.num_q_heads * w.head_dim * esize * 2 \
+    B_dec = (distinct if np.all(dec) else int(ctx[dec].sum())) * e_kv \
+        + int(dec.sum()) * w.num_q_heads * w.head_dim * esize * 2 \
         + int(nblk[dec].sum()) * 4 + 4 * int(dec.sum()) + (scale_bytes if np.all(dec) else 0)
     reshape = 2 * T * w.num_kv_heads * w.head_dim * esize * 2     # read the new rows, write them
     if fp8_pages:
@@ -115,7 +132,7 @@ def algorithmic_work(w, fp8_pages=False):
         reshape = 2 * w.num_kv_heads * (T * w.head_dim * esize + 2 * rows * w.head_dim
                                         + pages * 8)
     return dict(bytes=B, flops_prefill=F_pre, flops_decode=F_dec, bytes_decode=B_dec,
-                reshape_bytes=reshape)
+                reshape_bytes=reshape, logical_kv_bytes=int(ctx.sum()) * e_kv)
 
 
 class Runner:
@@ -138,7 +155,10 @@ class Runner:
         self.ctx_host = w.ctx_lens.astype(np.int32)
         self.params = pa.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                      **self.tiling)
-        first = pa.build_task_table(self.params, self.cu_host, self.ctx_host)
+        # a host copy of the block table lets the decomposer find shared prefixes
+        self.bt_host = w.block_table if self.params.shared_min else None
+        first = pa.build_task_table(self.params, self.cu_host, self.ctx_host,
+                                    block_table=self.bt_host)
         self.balance = (first.balance_snake, first.balance_modulo)
         self.num_tasks, self.num_combines = len(first.tasks), len(first.combines)
         self.num_partials = first.num_partials
@@ -171,7 +191,7 @@ class Runner:
             self.slot_ev[k].synchronize()      # the slot's previous copy and kernels are done
         pin = self.pin[k].numpy()
         t = pa.build_task_table(self.params, self.cu_host, self.ctx_host, pin[:self.cap_t],
-                                pin[self.cap_t:], with_balance=False)
+                                pin[self.cap_t:], with_balance=False, block_table=self.bt_host)
         nt, nc = len(t.tasks), len(t.combines)
         n = self.cap_t + nc
         with torch.cuda.stream(self.copy_stream):
@@ -260,7 +280,8 @@ class Runner:
         for _ in range(reps):
             t0 = time.perf_counter()
             self.pa.build_task_table(self.params, self.cu_host, self.ctx_host, pin[:self.cap_t],
-                                     pin[self.cap_t:], with_balance=False)
+                                     pin[self.cap_t:], with_balance=False,
+                                     block_table=self.bt_host)
             ts.append(time.perf_counter() - t0)
         return float(np.median(ts) * 1e6)
 
@@ -290,7 +311,7 @@ def cpu_baseline(name, budget_s=12.0):
     import synth
     from oracle import attention as oa
     from oracle import cache as oc
-    w = synth.make_workload(name)
+    w = synth.make_workload(name.split(":")[0])
     rng = np.random.default_rng(0)
     order = rng.permutation(w.num_seqs)
     vals = synth.make_values(w, device="cuda", nan_sentinels=False)
@@ -417,6 +438,8 @@ def main():
             res["attn_gbs"] = round(wk["bytes"] / t_launch / 1e9, 1)
             res["attn_tflops_prefill"] = round(wk["flops_prefill"] / t_launch / 1e12, 2)
             res["hbm_frac"] = round(res["attn_gbs"] / HBM_PEAK_GBS, 4)
+            # K/V bytes as every sequence sees them (aliased prefix rows once per sequence)
+            res["logical_kv_gbs"] = round(wk["logical_kv_bytes"] / t_launch / 1e9, 1)
             res["mfma_frac"] = round(res["attn_tflops_prefill"] / MFMA_BF16_PEAK_TFLOPS, 4)
             res["roofline_frac"] = round(max(wk["bytes"] / (HBM_PEAK_GBS * 1e9),
                                              wk["flops_prefill"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
@@ -435,7 +458,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload)
     import synth
-    wl = synth.make_workload(args.workload)
+    wl = synth.make_workload(args.workload.split(":")[0])
     traffic = counter_traffic(args.workload, head["tiling"])
     line = {
         "metric": METRIC,

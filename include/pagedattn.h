@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 enum pa_status {
   PA_OK = 0,
@@ -68,7 +68,12 @@ enum pa_status {
 
 enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 };
 
-enum pa_task_kind { PA_TASK_DECODE = 0, PA_TASK_PREFILL = 1, PA_TASK_VERIFY = 2 };
+enum pa_task_kind {
+  PA_TASK_DECODE = 0,
+  PA_TASK_PREFILL = 1,
+  PA_TASK_VERIFY = 2,
+  PA_TASK_SHARED = 3
+};
 
 /* One unit of attention work (8 x int32 = 32 bytes).
  *   kind    PA_TASK_DECODE: the single query row of sequence `seq`, all Hq/Hkv query heads of
@@ -80,6 +85,13 @@ enum pa_task_kind { PA_TASK_DECODE = 0, PA_TASK_PREFILL = 1, PA_TASK_VERIFY = 2 
  *           decode and verify alike) for all Hq/Hkv query heads of kv head `head`, keys
  *           [kv0, kv1) minus the causal mask; q_row0 = 0. Only paged_attn_varlen_prefill runs
  *           these tasks.
+ *           PA_TASK_SHARED: keys [kv0, kv1) of a prefix that q_rows consecutive decode
+ *           sequences seq .. seq+q_rows-1 hold in the same physical blocks (XY-Serve page,
+ *           automatic prefix cache; ATB page, KV cache reuse), for their single query rows and
+ *           all Hq/Hkv query heads of kv head `head`: the pages are read once for all of them.
+ *           Always writes partials: member i, head j goes to row partial + i*q_row0 + j (q_row0
+ *           holds the member stride). paged_attn_decode and paged_attn_varlen_prefill run
+ *           these tasks; paged_attn_decode_fp8 does not.
  *   partial -1: the task sees all keys its rows need and writes `out` directly.
  *           >= 0: first workspace row of this task's partial result (one row per
  *           (query row, head) pair it covers); split_combine merges the partials. */
@@ -106,11 +118,14 @@ typedef struct pa_combine {
  *   verify_rows   0 (off) or 2..16: a sequence with 2 <= q_len <= verify_rows and
  *                 (Hq/Hkv) * q_len <= 16 becomes verify tasks (key splits of dec_split per kv
  *                 head, all its rows and heads in one task) instead of prefill tiles
+ *   shared_min    0 (off) or a positive multiple of 64: neighbouring decode sequences whose
+ *                 block tables share at least this many leading keys in the same physical
+ *                 blocks form a shared-prefix group (build_task_table_shared only)
  *   reserved      must be 0 */
 typedef struct pa_params {
   int32_t num_q_heads, num_kv_heads, head_dim, block_size;
   int32_t dec_split, pf_q_tile, pf_kv_split, num_workers;
-  int32_t decode_weight, verify_rows, reserved[2];
+  int32_t decode_weight, verify_rows, shared_min, reserved;
 } pa_params;
 
 /* ABI version of the loaded library (PA_ABI_VERSION when headers and library match). */
@@ -142,13 +157,41 @@ int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu_seqlens);
  *   {min/max of per-worker load sums when the sorted tasks are dealt in a snake order,
  *    the same when dealt by i % num_workers} (XY-Serve page, section 4.4, load-balance report).
  *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (heads or tiling parameters), PA_ERR_BLOCK_SIZE,
- *   PA_ERR_INPUT (cu[0] != 0, a q_len < 1, a context shorter than its rows),
- *   PA_ERR_CAPACITY. Pure, deterministic, thread-safe, no HIP calls. */
+ *   PA_ERR_INPUT (cu[0] != 0, a q_len < 1, a context shorter than its rows, shared_min > 0
+ *   here), PA_ERR_CAPACITY. Pure, deterministic, thread-safe, no HIP calls. */
 int build_task_table(const pa_params* params, const int32_t* cu_seqlens_q_host,
                      const int32_t* context_lens_host, int32_t num_seqs, pa_task* tasks,
                      int32_t tasks_cap, int32_t* num_tasks, pa_combine* combines,
                      int32_t combines_cap, int32_t* num_combines, int32_t* num_partials,
                      double* balance);
+
+/* build_task_table plus shared-prefix groups, from a host copy of the block table
+ * [num_seqs, max_blocks_per_seq] (XY-Serve page, automatic prefix cache; ATB page, KV cache
+ * reuse: sequences that repeat a prefix reuse its cached blocks).
+ *   Two neighbouring decode sequences (q_len 1, in batch order) share the leading logical
+ *   blocks whose physical ids are equal, among the blocks both need; their shared keys are
+ *   those blocks' keys rounded down to a multiple of 64. A maximal run of neighbours sharing
+ *   at least params->shared_min keys pairwise is a group with shared length L (the smallest
+ *   pairwise value); groups form only when Hq/Hkv <= 8. A group of n is cut into
+ *   ceil(n / (16 / G)) column sets of consecutive members with sizes as equal as possible. Per
+ *   kv head and set: PA_TASK_SHARED tasks over [0, L) in pieces of dec_split (columns =
+ *   (member, query head)), and PA_TASK_DECODE tasks over each member's keys [L, ctx) in pieces
+ *   of dec_split. Member i of a set owns W = (S + max U) * G partial rows from base + i*W (S
+ *   shared pieces, U_i own pieces; piece k's rows at + k*G) and one combine record with
+ *   S + U_i slots; rows beyond a member's own pieces are left unused. Emission order for a
+ *   group (at its first member): kv head, set, the set's combine records, its shared pieces,
+ *   then each member's pieces. Everything else as build_task_table.
+ *   With shared_min = 0 the result equals build_task_table's (block_table may then be NULL).
+ *   Errors: as build_task_table; PA_ERR_NULL (block_table NULL with shared_min > 0),
+ *   PA_ERR_SHAPE (a context needs more than max_blocks_per_seq blocks), PA_ERR_INPUT (a block
+ *   shared by two neighbours receives either one's new row: logical block (ctx-1)/block_size
+ *   must stay private). */
+int build_task_table_shared(const pa_params* params, const int32_t* cu_seqlens_q_host,
+                            const int32_t* context_lens_host, int32_t num_seqs,
+                            const int32_t* block_table_host, int32_t max_blocks_per_seq,
+                            pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                            pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
+                            int32_t* num_partials, double* balance);
 
 /* Workspace bytes for `num_partials` partial rows of head_dim D (fp32 accumulator row plus
  * running max and sum), rounded up to 256 bytes. 0 when num_partials <= 0. */
@@ -172,10 +215,10 @@ int reshape_and_cache(const void* k_new, const void* v_new, void* k_pages, void*
 
 /* Decode attention: one query token per sequence (MindIE page, "Continuous Batching": each
  * step decodes one token per request), q [num_seqs, Hq, D] -> out [num_seqs, Hq, D].
- * Runs the decode tasks of a table built with cu_seqlens_q = 0, 1, ..., num_seqs (copied to
- * the device by the caller: tasks_dev [num_tasks], combines_dev [num_combines]), then merges
- * split partials with a log-sum-exp combine. Each KV page is read once for all query heads of
- * its kv head.
+ * Runs the decode and shared-prefix tasks of a table built with cu_seqlens_q = 0, 1, ...,
+ * num_seqs (copied to the device by the caller: tasks_dev [num_tasks], combines_dev
+ * [num_combines]), then merges split partials with a log-sum-exp combine. Each KV page is read
+ * once for all query heads of its kv head, and a shared prefix once for its group's members.
  *   workspace: device buffer of at least pa_workspace_bytes(num_partials, D) bytes
  *   (may be NULL when num_combines == 0).
  *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (Hq % Hkv, Hq/Hkv > 16, D), PA_ERR_BLOCK_SIZE,

@@ -50,10 +50,10 @@ def pack_seqlens(lengths) -> np.ndarray:
 
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, dec_split=512, pf_q_tile=128,
-                pf_kv_split=0, num_workers=256, decode_weight=1, verify_rows=0) -> PaParams:
+                pf_kv_split=0, num_workers=256, decode_weight=1, verify_rows=0,
+                shared_min=0) -> PaParams:
     return PaParams(num_q_heads, num_kv_heads, head_dim, block_size, dec_split, pf_q_tile,
-                    pf_kv_split, num_workers, decode_weight, verify_rows,
-                    (ctypes.c_int32 * 2)(0, 0))
+                    pf_kv_split, num_workers, decode_weight, verify_rows, shared_min, 0)
 
 
 @dataclass
@@ -66,36 +66,45 @@ class TaskTable:
 
 
 def build_task_table(params: PaParams, cu_seqlens_q, context_lens, tasks_out=None,
-                     combines_out=None, with_balance=True) -> TaskTable:
+                     combines_out=None, with_balance=True, block_table=None) -> TaskTable:
     """Host task table (library call).
 
     Without output buffers the table is sized with a first call (PA_ERR_CAPACITY) and filled
     by a second. With ``tasks_out`` / ``combines_out`` (int32 [cap, 8] numpy arrays, e.g. views
     of pinned host memory) it is one call that writes into them; the returned TaskTable then
-    holds views of the filled rows.
+    holds views of the filled rows. A host ``block_table`` ([N, max_blocks]) selects
+    build_task_table_shared, which groups decode sequences that share leading blocks when
+    ``params.shared_min`` > 0.
     """
     L = lib()
     cu = _i32(cu_seqlens_q)
     ctx = _i32(context_lens)
     n = ctx.shape[0]
+    if block_table is None:
+        fn, name, head = L.build_task_table, "build_task_table", []
+    else:
+        bt = _i32(block_table)
+        if bt.ndim != 2 or bt.shape[0] != n:
+            raise ValueError("block_table must be [num_seqs, max_blocks]")
+        fn, name, head = L.build_task_table_shared, "build_task_table_shared", \
+            [_ptr(bt), bt.shape[1]]
     nt, nc, npart = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     bal = (ctypes.c_double * 2)() if with_balance else None
     if tasks_out is None:
-        rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, None, 0,
-                                ctypes.byref(nt), None, 0, ctypes.byref(nc),
-                                ctypes.byref(npart), None)
+        rc = fn(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, *head, None, 0, ctypes.byref(nt),
+                None, 0, ctypes.byref(nc), ctypes.byref(npart), None)
         if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
-            check(rc, "build_task_table")
+            check(rc, name)
         tasks_out = np.zeros((nt.value, 8), dtype=np.int32)
         combines_out = np.zeros((nc.value, 8), dtype=np.int32)
     for a in (tasks_out, combines_out):
         if a.dtype != np.int32 or a.ndim != 2 or a.shape[1] != 8 or not a.flags.c_contiguous:
             raise ValueError("table buffers must be contiguous int32 [cap, 8]")
-    rc = L.build_task_table(ctypes.byref(params), _ptr(cu), _ptr(ctx), n,
-                            tasks_out.ctypes.data_as(ctypes.POINTER(PaTask)), tasks_out.shape[0],
-                            ctypes.byref(nt), combines_out.ctypes.data_as(ctypes.POINTER(PaCombine)),
-                            combines_out.shape[0], ctypes.byref(nc), ctypes.byref(npart), bal)
-    check(rc, "build_task_table")
+    rc = fn(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, *head,
+            tasks_out.ctypes.data_as(ctypes.POINTER(PaTask)), tasks_out.shape[0],
+            ctypes.byref(nt), combines_out.ctypes.data_as(ctypes.POINTER(PaCombine)),
+            combines_out.shape[0], ctypes.byref(nc), ctypes.byref(npart), bal)
+    check(rc, name)
     return TaskTable(tasks_out[:nt.value], combines_out[:nc.value], npart.value,
                      bal[0] if bal is not None else float("nan"),
                      bal[1] if bal is not None else float("nan"))
@@ -302,7 +311,8 @@ class StepPlan:
         self.cu_host = pack_seqlens(q_lens)
         self.ctx_host = _i32(context_lens)
         self.params = make_params(num_q_heads, num_kv_heads, head_dim, block_size, **tiling)
-        self.table = build_task_table(self.params, self.cu_host, self.ctx_host)
+        self.table = build_task_table(self.params, self.cu_host, self.ctx_host,
+                                      block_table=block_table if self.params.shared_min else None)
         self.head_dim = head_dim
         self.device = device
         self.cu = torch.from_numpy(self.cu_host).to(device)
@@ -326,6 +336,8 @@ class StepPlan:
         if not self.decode_only or self.params.verify_rows:
             raise ValueError(f"{who} runs decode tasks only: every q_len must be 1 and "
                              "verify_rows 0 (use varlen for other batches)")
+        if who == "decode_fp8" and self.params.shared_min:
+            raise ValueError("decode_fp8 runs no shared-prefix tasks: build with shared_min 0")
 
     def decode(self, q, k_pages, v_pages, scale, out, stream=None):
         self._check_decode_table("decode")

@@ -24,7 +24,8 @@ PA_FP32 = 1
 PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
-ABI_VERSION = 3
+PA_TASK_SHARED = 3
+ABI_VERSION = 4
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -36,7 +37,8 @@ ERROR_NAMES = {
 EXPORTS = ("pa_abi_version", "pa_last_error", "pa_pack_seqlens", "build_task_table",
            "pa_workspace_bytes", "reshape_and_cache", "paged_attn_decode",
            "paged_attn_varlen_prefill", "pa_validate_block_table", "reshape_and_cache_fp8",
-           "paged_attn_decode_fp8")
+           "paged_attn_decode_fp8",
+           "build_task_table_shared")
 
 
 class PaTask(ctypes.Structure):
@@ -52,8 +54,8 @@ class PaCombine(ctypes.Structure):
 class PaParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("num_q_heads", "num_kv_heads", "head_dim", "block_size", "dec_split",
-                 "pf_q_tile", "pf_kv_split", "num_workers", "decode_weight", "verify_rows")] + \
-               [("reserved", ctypes.c_int32 * 2)]
+                 "pf_q_tile", "pf_kv_split", "num_workers", "decode_weight", "verify_rows",
+                 "shared_min", "reserved")]
 
 
 class PagedAttnError(RuntimeError):
@@ -87,6 +89,11 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(PaTask), i32, pi32,
                                    ctypes.POINTER(PaCombine), i32, pi32, pi32,
                                    ctypes.POINTER(ctypes.c_double)]
+    L.build_task_table_shared.restype = ctypes.c_int
+    L.build_task_table_shared.argtypes = [ctypes.POINTER(PaParams), pi32, pi32, i32, pi32, i32,
+                                          ctypes.POINTER(PaTask), i32, pi32,
+                                          ctypes.POINTER(PaCombine), i32, pi32, pi32,
+                                          ctypes.POINTER(ctypes.c_double)]
     L.pa_workspace_bytes.restype = ctypes.c_size_t
     L.pa_workspace_bytes.argtypes = [i32, i32]
     L.reshape_and_cache.restype = ctypes.c_int

@@ -24,6 +24,7 @@
 // tile j are, and the value product of tile j runs beside the maximum of tile j+1.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -163,7 +164,10 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
       else
         static_cast<float*>(a.out)[o] = v;
     } else {
-      const size_t row = static_cast<size_t>(t.partial) + h;
+      // shared-prefix tasks: member h / G's rows start q_row0 (the member stride) apart
+      const int mem = h / G;
+      const size_t row = static_cast<size_t>(t.partial) +
+                         (t.kind == PA_TASK_SHARED ? mem * t.q_row0 + (h - mem * G) : h);
       a.ws_acc[row * D + d] = A;
       if (d == 0) {
         a.ws_ml[2 * row] = M;
@@ -184,7 +188,9 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
   const int s = t.seq, kvh = t.head;
   const int tok = a.cu_seqlens ? a.cu_seqlens[s] : s;
   const int bs = a.block_size;
-  const int nrows = t.q_rows;                      // 1 for decode, the draft rows for verify
+  // rows: 1 for decode, the draft rows for verify, the members (consecutive decode rows, so
+  // member r's row is tok + r) for a shared-prefix task
+  const int nrows = t.q_rows;
   const int ncol = nrows * G;
   const int row = i16 / G, hh = i16 - row * G;     // this lane's score column
 
@@ -201,9 +207,12 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
     }
   }
   // causal limit of this column: its row sits at position ctx - nrows + row and sees the keys
-  // before that position and the key at it (for decode: every key)
-  const int key_lim = a.context_lens[s] - nrows + row + 1;
-  const int lim_lo = a.context_lens[s] - nrows + 1;  // smallest limit over the task's rows
+  // before that position and the key at it (for decode: every key). A shared-prefix task's
+  // rows are single decode rows of its members, and its keys lie below every member's own
+  // row: no limit.
+  const bool shared = t.kind == PA_TASK_SHARED;
+  const int key_lim = shared ? INT_MAX : a.context_lens[s] - nrows + row + 1;
+  const int lim_lo = shared ? INT_MAX : a.context_lens[s] - nrows + 1;
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
@@ -536,15 +545,19 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
   const int s = t.seq, kvh = t.head;
   const int tok = a.cu_seqlens ? a.cu_seqlens[s] : s;
   const int bs = a.block_size;
+  // columns: the G heads of one decode row, or (member, head) pairs of a shared-prefix task
+  // (members are consecutive decode rows, so member r's row is tok + r)
+  const int ncol = t.q_rows * G;
+  const int row = i16 / G, hh = i16 - row * G;
 
   f32x4 qf[KQ];
   {
     const float* qp = static_cast<const float*>(a.q) +
-                      (static_cast<size_t>(tok) * a.num_q_heads + kvh * G + i16) * D + 4 * g4;
+                      (static_cast<size_t>(tok + row) * a.num_q_heads + kvh * G + hh) * D + 4 * g4;
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (i16 < G) v = *reinterpret_cast<const f32x4*>(qp + 16 * kq);
+      if (i16 < ncol) v = *reinterpret_cast<const f32x4*>(qp + 16 * kq);
       qf[kq] = v;
     }
   }
@@ -619,7 +632,7 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
       for (int n = 0; n < VEC; ++n)
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[r][n], p[r], acc[n], 0, 0, 0);
   }
-  decode_merge_and_store<D>(a, t, tok, G, G, m, l, acc, smem, false);
+  decode_merge_and_store<D>(a, t, tok, G, ncol, m, l, acc, smem, false);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1132,7 +1145,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   __shared__ float smem[128 + 4 * 16 * D];
   const pa_task t = a.tasks[blockIdx.x];
-  if (t.kind != PA_TASK_DECODE) return;
+  if (t.kind != PA_TASK_DECODE && t.kind != PA_TASK_SHARED) return;
   if constexpr (sizeof(T) == 2)
     decode_task_bf16<D>(a, t, smem);
   else

@@ -72,8 +72,10 @@ int check_params(const pa_params* p) {
   if (p->verify_rows != 0 && (p->verify_rows < 2 || p->verify_rows > pa::kMaxGroup))
     return set_error(PA_ERR_SHAPE, "verify_rows %d must be 0 or lie in [2, %d]", p->verify_rows,
                      pa::kMaxGroup);
-  if (p->reserved[0] != 0 || p->reserved[1] != 0)
-    return set_error(PA_ERR_SHAPE, "pa_params.reserved must be zero");
+  if (p->shared_min < 0 || p->shared_min % pa::kSplitQuantum)
+    return set_error(PA_ERR_SHAPE, "shared_min %d must be 0 or a positive multiple of %d",
+                     p->shared_min, pa::kSplitQuantum);
+  if (p->reserved != 0) return set_error(PA_ERR_SHAPE, "pa_params.reserved must be zero");
   return PA_OK;
 }
 
@@ -104,20 +106,80 @@ int64_t tile_pairs(int64_t e0, int64_t e1, int64_t kv0, int64_t kv1) {
   return total;
 }
 
+// Shared-prefix group of decode sequences first .. first+n-1 with shared length L (keys):
+// per kv head and column set, the set's combine records, its shared pieces over [0, L), then
+// each member's own pieces over [L, ctx). Member i of a set owns W = (S + max U) * G partial
+// rows from base + i*W; piece k of a member sits at + k*G.
+template <class EmitF, class CombF>
+void emit_group(int32_t first, int32_t n, int32_t L, const int32_t* ctx, int32_t Hkv, int32_t G,
+                int32_t dec_split, int64_t weight, EmitF& emit, CombF& combine, int64_t& parts) {
+  const int32_t columns = pa::kMaxGroup / G;
+  const int32_t nsets = static_cast<int32_t>(ceil_div(n, columns));
+  const int64_t S = ceil_div(L, dec_split);
+  for (int32_t g = 0; g < Hkv; ++g) {
+    int32_t m0 = first;
+    for (int32_t set = 0; set < nsets; ++set) {
+      const int32_t size = n / nsets + (set < n % nsets ? 1 : 0);
+      int64_t umax = 0;
+      for (int32_t i = 0; i < size; ++i) umax = std::max(umax, ceil_div(ctx[m0 + i] - L, dec_split));
+      const int64_t W = (S + umax) * G;
+      const int64_t base = parts;
+      parts += size * W;
+      for (int32_t i = 0; i < size; ++i) {
+        const int32_t U = static_cast<int32_t>(ceil_div(ctx[m0 + i] - L, dec_split));
+        combine(pa_combine{m0 + i, 0, 1, g * G, G, static_cast<int32_t>(base + i * W),
+                           static_cast<int32_t>(S) + U, 0});
+      }
+      for (int64_t k = 0; k < S; ++k) {
+        const int32_t kv0 = static_cast<int32_t>(k * dec_split);
+        const int32_t kv1 = std::min(L, kv0 + dec_split);
+        emit(int64_t(kv1 - kv0) * size * G * weight,
+             pa_task{PA_TASK_SHARED, m0, g, static_cast<int32_t>(W), size, kv0, kv1,
+                     static_cast<int32_t>(base + k * G)});
+      }
+      for (int32_t i = 0; i < size; ++i) {
+        const int32_t m = m0 + i;
+        const int64_t U = ceil_div(ctx[m] - L, dec_split);
+        for (int64_t j = 0; j < U; ++j) {
+          const int32_t kv0 = L + static_cast<int32_t>(j * dec_split);
+          const int32_t kv1 = std::min(ctx[m], kv0 + dec_split);
+          emit(int64_t(kv1 - kv0) * G * weight,
+               pa_task{PA_TASK_DECODE, m, g, 0, 1, kv0, kv1,
+                       static_cast<int32_t>(base + i * W + (S + j) * G)});
+        }
+      }
+      m0 += size;
+    }
+  }
+}
+
 // Emission order of the decomposition: sequences ascending; decode and verify sequences give
-// kv head, then key split; prefill sequences give query head, then query tile, then key split.
-// `emit(load, task)` and `combine(record)` receive every item in that order, and the partial
-// rows are numbered in the same order.
+// kv head, then key split; prefill sequences give query head, then query tile, then key split;
+// a shared-prefix group is emitted at its first member (emit_group). `emit(load, task)` and
+// `combine(record)` receive every item in that order, and the partial rows are numbered in the
+// same order. `pair` (NULL without sharing) holds, for s >= 1, the keys decode sequences s-1
+// and s share.
 template <class EmitF, class CombF>
 void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
-               EmitF&& emit, CombF&& combine, int64_t* num_partials) {
+               const int32_t* pair, EmitF&& emit, CombF&& combine, int64_t* num_partials) {
   // parameters in locals: the stores of emitted records could otherwise alias them
   const int32_t Hq = p->num_q_heads, Hkv = p->num_kv_heads, G = Hq / Hkv;
   const int32_t dec_split = p->dec_split, q_tile = p->pf_q_tile, kv_split = p->pf_kv_split;
   const int64_t weight = p->decode_weight;
   const int32_t verify_rows = p->verify_rows;
+  const int32_t shared_min = p->shared_min;
+  const bool sharing = pair && shared_min > 0 && pa::kMaxGroup / G >= 2;
   int64_t parts = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
+    if (sharing) {
+      int32_t end = s, L = INT32_MAX;
+      while (end + 1 < num_seqs && pair[end + 1] >= shared_min) L = std::min(L, pair[++end]);
+      if (end > s) {
+        emit_group(s, end - s + 1, L, ctx, Hkv, G, dec_split, weight, emit, combine, parts);
+        s = end;
+        continue;
+      }
+    }
     const int32_t ql = cu[s + 1] - cu[s];
     const int32_t keys = ctx[s];
     const int64_t prefix = static_cast<int64_t>(keys) - ql;
@@ -172,37 +234,15 @@ void decompose(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_
   *num_partials = parts;
 }
 
-// Task, combine and partial-row counts without emitting anything.
+// Task, combine and partial-row counts: the decomposition with counting callbacks.
 void count(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
-           int64_t* nt, int64_t* nc, int64_t* np) {
-  const int64_t G = p->num_q_heads / p->num_kv_heads;
-  int64_t t = 0, c = 0, parts = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t ql = cu[s + 1] - cu[s];
-    const int64_t prefix = static_cast<int64_t>(ctx[s]) - ql;
-    if (ql == 1 || verify_seq(ql, static_cast<int32_t>(G), p->verify_rows)) {
-      const int64_t nsplit = ceil_div(ctx[s], p->dec_split);
-      t += nsplit * p->num_kv_heads;
-      if (nsplit > 1) {
-        c += p->num_kv_heads;
-        parts += nsplit * G * ql * p->num_kv_heads;
-      }
-    } else {
-      for (int32_t r0 = 0; r0 < ql; r0 += p->pf_q_tile) {
-        const int64_t rows = std::min(p->pf_q_tile, ql - r0);
-        const int64_t lim = prefix + r0 + rows;
-        const int64_t nsplit = p->pf_kv_split > 0 ? ceil_div(lim, p->pf_kv_split) : 1;
-        t += nsplit * p->num_q_heads;
-        if (nsplit > 1) {
-          c += p->num_q_heads;
-          parts += nsplit * rows * p->num_q_heads;
-        }
-      }
-    }
-  }
+           const int32_t* pair, int64_t* nt, int64_t* nc, int64_t* np) {
+  int64_t t = 0, c = 0;
+  decompose(
+      p, cu, ctx, num_seqs, pair, [&](int64_t, const pa_task&) { ++t; },
+      [&](const pa_combine&) { ++c; }, np);
   *nt = t;
   *nc = c;
-  *np = parts;
 }
 
 // Stable order of n loads, descending: an LSD radix sort on keys that hold (max_load - load)
@@ -269,11 +309,11 @@ Scratch& scratch() {
 
 }  // namespace
 
-// Dynamic Decomposer + load-sorted reorder (XY-Serve page, sections 2.2 and 4.4).
-extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int32_t* ctx,
-                                int32_t num_seqs, pa_task* tasks, int32_t tasks_cap,
-                                int32_t* num_tasks, pa_combine* combines, int32_t combines_cap,
-                                int32_t* num_combines, int32_t* num_partials, double* balance) {
+namespace {
+
+int check_table_inputs(const pa_params* p, const int32_t* cu, const int32_t* ctx,
+                       int32_t num_seqs, const int32_t* num_tasks, const int32_t* num_combines,
+                       const int32_t* num_partials) {
   if (!p || !cu || (num_seqs > 0 && !ctx) || !num_tasks || !num_combines || !num_partials)
     return set_error(PA_ERR_NULL, "build_task_table: NULL pointer");
   if (int rc = check_params(p)) return rc;
@@ -286,8 +326,80 @@ extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int
       return set_error(PA_ERR_INPUT, "context_lens[%d] = %d is shorter than its %d query rows",
                        s, ctx[s], cu[s + 1] - cu[s]);
   }
+  return PA_OK;
+}
+
+int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
+                const int32_t* pair, pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
+                int32_t* num_partials, double* balance);
+
+}  // namespace
+
+// Dynamic Decomposer + load-sorted reorder (XY-Serve page, sections 2.2 and 4.4).
+extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int32_t* ctx,
+                                int32_t num_seqs, pa_task* tasks, int32_t tasks_cap,
+                                int32_t* num_tasks, pa_combine* combines, int32_t combines_cap,
+                                int32_t* num_combines, int32_t* num_partials, double* balance) {
+  if (int rc = check_table_inputs(p, cu, ctx, num_seqs, num_tasks, num_combines, num_partials))
+    return rc;
+  if (p->shared_min > 0)
+    return set_error(PA_ERR_INPUT,
+                     "shared_min > 0 needs the block table: call build_task_table_shared");
+  return build_table(p, cu, ctx, num_seqs, nullptr, tasks, tasks_cap, num_tasks, combines,
+                     combines_cap, num_combines, num_partials, balance);
+}
+
+// The same plus shared-prefix groups (XY-Serve page, automatic prefix cache; ATB page, KV cache
+// reuse), found from a host copy of the block table.
+extern "C" int build_task_table_shared(const pa_params* p, const int32_t* cu, const int32_t* ctx,
+                                       int32_t num_seqs, const int32_t* bt, int32_t width,
+                                       pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                                       pa_combine* combines, int32_t combines_cap,
+                                       int32_t* num_combines, int32_t* num_partials,
+                                       double* balance) {
+  if (int rc = check_table_inputs(p, cu, ctx, num_seqs, num_tasks, num_combines, num_partials))
+    return rc;
+  if (p->shared_min == 0)
+    return build_table(p, cu, ctx, num_seqs, nullptr, tasks, tasks_cap, num_tasks, combines,
+                       combines_cap, num_combines, num_partials, balance);
+  if (num_seqs > 0 && !bt)
+    return set_error(PA_ERR_NULL, "build_task_table_shared: block_table is NULL");
+  const int32_t bs = p->block_size;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if ((ctx[s] + bs - 1) / bs > width)
+      return set_error(PA_ERR_SHAPE, "seq %d needs %d blocks, table has %d columns", s,
+                       (ctx[s] + bs - 1) / bs, width);
+  // keys that decode neighbours s-1 and s read from the same physical blocks
+  static thread_local std::vector<int32_t> pair;
+  pair.assign(static_cast<size_t>(std::max(num_seqs, 1)), 0);
+  for (int32_t s = 1; s < num_seqs; ++s) {
+    if (cu[s + 1] - cu[s] != 1 || cu[s] - cu[s - 1] != 1) continue;
+    const int32_t need = std::min((ctx[s - 1] + bs - 1) / bs, (ctx[s] + bs - 1) / bs);
+    const int32_t* a = bt + static_cast<int64_t>(s - 1) * width;
+    const int32_t* b = bt + static_cast<int64_t>(s) * width;
+    int32_t common = 0;
+    while (common < need && a[common] == b[common]) ++common;
+    // logical block (ctx-1)/bs receives the sequence's new row in this step
+    if (common > std::min((ctx[s - 1] - 1) / bs, (ctx[s] - 1) / bs))
+      return set_error(PA_ERR_INPUT,
+                       "sequences %d and %d share block_table[.][%d] = %d, which receives a "
+                       "new row", s - 1, s, std::min((ctx[s - 1] - 1) / bs, (ctx[s] - 1) / bs),
+                       a[std::min((ctx[s - 1] - 1) / bs, (ctx[s] - 1) / bs)]);
+    pair[s] = static_cast<int32_t>(int64_t(common) * bs / pa::kSplitQuantum * pa::kSplitQuantum);
+  }
+  return build_table(p, cu, ctx, num_seqs, pair.data(), tasks, tasks_cap, num_tasks, combines,
+                     combines_cap, num_combines, num_partials, balance);
+}
+
+namespace {
+
+int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
+                const int32_t* pair, pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
+                int32_t* num_partials, double* balance) {
   int64_t nt = 0, nc = 0, np = 0;
-  count(p, cu, ctx, num_seqs, &nt, &nc, &np);
+  count(p, cu, ctx, num_seqs, pair, &nt, &nc, &np);
   if (nt > INT32_MAX || nc > INT32_MAX || np > INT32_MAX)
     return set_error(PA_ERR_SHAPE, "task table exceeds int32 indexing");
   *num_tasks = static_cast<int32_t>(nt);
@@ -314,7 +426,7 @@ extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int
   int64_t nti = 0, nci = 0, parts = 0;
   int64_t mn = INT64_MAX, mx = 0;
   decompose(
-      p, cu, ctx, num_seqs,
+      p, cu, ctx, num_seqs, pair,
       [&](int64_t load, const pa_task& t) {
         if (nti < nt) {
           loads[nti] = load;
@@ -359,6 +471,8 @@ extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int
   }
   return pa::clear_error();
 }
+
+}  // namespace
 
 extern "C" size_t pa_workspace_bytes(int32_t num_partials, int32_t head_dim) {
   if (num_partials <= 0 || head_dim <= 0) return 0;

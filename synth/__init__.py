@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_workload", "deal_block_table", "make_values",
-           "make_fp8_pages", "custom_workload"]
+           "make_fp8_pages", "custom_workload", "shared_prefix_workload"]
 
 
 @dataclass
@@ -126,6 +126,7 @@ WORKLOADS = {
     "mixed_bf16": 5,
     "verify_gqa_bf16": 6,
     "decode_mha_fp8": 2,
+    "decode_shared_mha_bf16": 7,
 }
 
 
@@ -133,6 +134,14 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
     """Build the integer side of a named synthetic workload (lengths + block table)."""
     seed = WORKLOADS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
+    if name == "decode_shared_mha_bf16":
+        # agent-style serving: 8 prompts, each repeated by 16 requests that now decode; a prompt
+        # of U[1024, 8192] keys (whole blocks) is cached once, and every request has
+        # U[16, 512] keys of its own after it
+        prefix = rng.integers(64, 513, size=8) * 16
+        own = rng.integers(16, 513, size=(8, 16))
+        return shared_prefix_workload(prefix, own, 32, 32, 128, 16, seed=seed, name=name,
+                                      rng=rng)
     q, ctx, hq, hkv, d, bs, dt, pool = _lengths(name, rng)
     table, nb = deal_block_table(ctx, bs, rng, pool_blocks=pool)
     return Workload(name, seed, q, ctx, hq, hkv, d, bs, dt, table, nb)
@@ -149,6 +158,46 @@ def custom_workload(q_lens, ctx_lens, num_q_heads, num_kv_heads, head_dim, block
                                  min_width=min_width)
     return Workload(name, seed, q, ctx, num_q_heads, num_kv_heads, head_dim, block_size,
                     dtype, table, nb)
+
+
+def shared_prefix_workload(prefix_lens, own_lens, num_q_heads, num_kv_heads, head_dim,
+                           block_size, dtype="bf16", seed=0, name="shared", rng=None,
+                           spare_blocks=0):
+    """Decode sequences in groups that share a cached prefix.
+
+    Group g's first prefix_lens[g] keys (a multiple of block_size) sit in blocks that every
+    member's table lists first; member m of group g then has own_lens[g][m] >= 1 keys of its
+    own in private blocks (the last of them is the row this step writes). Groups are laid out
+    one after another in batch order, members consecutively. Physical ids come from a seeded
+    permutation of the pool.
+    """
+    rng = np.random.default_rng(seed) if rng is None else rng
+    bs = block_size
+    prefix = [int(x) for x in prefix_lens]
+    own = [[int(x) for x in row] for row in own_lens]
+    if any(x % bs for x in prefix) or any(x < 1 for row in own for x in row):
+        raise ValueError("prefixes must be whole blocks and every member needs an own key")
+    need = sum(x // bs for x in prefix) + sum((x + bs - 1) // bs for row in own for x in row)
+    nb = need + spare_blocks
+    perm = rng.permutation(nb)
+    rows, ctx = [], []
+    pos = 0
+    for g, P in enumerate(prefix):
+        shared = perm[pos:pos + P // bs].tolist()
+        pos += P // bs
+        for x in own[g]:
+            k = (x + bs - 1) // bs
+            rows.append(shared + perm[pos:pos + k].tolist())
+            pos += k
+            ctx.append(P + x)
+    width = max(len(r) for r in rows)
+    table = np.full((len(rows), width), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        table[i, :len(r)] = r
+    q = np.ones(len(rows), dtype=np.int64)
+    return Workload(name, seed, q, np.asarray(ctx, dtype=np.int64), num_q_heads, num_kv_heads,
+                    head_dim, block_size, dtype, table, nb,
+                    extra={"prefix_lens": prefix, "own_lens": own})
 
 
 def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinels=True):

@@ -46,3 +46,46 @@ def check_close(got, ref, dtype, what=""):
     assert err.max() <= mx, f"{what}: max-abs {err.max():.3e} > {mx}"
     assert err.mean() <= mean, f"{what}: mean-abs {err.mean():.3e} > {mean}"
     return float(err.max()), float(err.mean())
+
+
+def aliased_batch(rng, bs, n_groups):
+    """Decode sequences in runs that share a random number of leading blocks, a prefill and a
+    verify sequence in between, and private blocks for everything else."""
+    rows, ctx, q = [], [], []
+    nxt = 1000
+    for g in range(n_groups):
+        shared = [nxt + i for i in range(int(rng.integers(0, 17)))]
+        nxt += len(shared)
+        for m in range(int(rng.integers(1, 6))):
+            c = len(shared) * bs + int(rng.integers(1, 200))
+            need = -(-c // bs)
+            row = shared + list(range(nxt, nxt + need - len(shared)))
+            nxt += need - len(shared)
+            rows.append(row)
+            ctx.append(c)
+            q.append(1)
+        if g % 2:
+            c = int(rng.integers(5, 90))
+            rows.append(list(range(nxt, nxt + -(-c // bs))))
+            nxt += -(-c // bs)
+            ctx.append(c)
+            q.append(int(rng.integers(2, 5)))
+    width = max(len(r) for r in rows)
+    bt = np.full((len(rows), width), -1, dtype=np.int64)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    return q, ctx, bt
+
+
+def aliased_workload(rng, bs, n_groups, num_q_heads, num_kv_heads, head_dim, dtype="bf16",
+                     seed=0, spare_blocks=2):
+    """aliased_batch as a synth.Workload: the block ids mapped onto a dense, shuffled pool."""
+    import synth
+    q, ctx, bt = aliased_batch(rng, bs, n_groups)
+    ids = np.unique(bt[bt >= 0])
+    nb = len(ids) + spare_blocks
+    new = rng.permutation(nb)[:len(ids)]
+    table = np.full(bt.shape, -1, dtype=np.int32)
+    table[bt >= 0] = new[np.searchsorted(ids, bt[bt >= 0])]
+    return synth.Workload("aliased", seed, np.asarray(q, np.int64), np.asarray(ctx, np.int64),
+                          num_q_heads, num_kv_heads, head_dim, bs, dtype, table, nb)

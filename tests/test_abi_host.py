@@ -13,6 +13,7 @@ import synth
 import paged_variable_length_amd as pa
 from paged_variable_length_amd import _abi
 from oracle import task_table as ot
+from tests.helpers import aliased_batch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -127,7 +128,7 @@ def test_task_table_errors_match_oracle():
 
 def test_reserved_params_must_be_zero():
     p = pa.make_params(2, 1, 64, 16)
-    p.reserved[1] = 3
+    p.reserved = 3
     with pytest.raises(pa.PagedAttnError) as e:
         pa.build_task_table(p, np.array([0, 1], np.int32), np.array([5], np.int32))
     assert e.value.code == _abi.PA_ERR_SHAPE
@@ -229,3 +230,79 @@ def test_step_plan_decode_refuses_non_decode_tables():
             plan.decode(q, q, q, 0.1, q)
         with pytest.raises(ValueError, match="decode tasks only"):
             plan.decode_fp8(q, q, q, q, q, 0.1, q)
+
+
+# ---- shared-prefix tables (build_task_table_shared) against the oracle ----
+
+def compare_shared(q_lens, ctx, bt, **kw):
+    hq, hkv, d, bs = kw.pop("hq"), kw.pop("hkv"), kw.pop("d", 128), kw.pop("bs")
+    cu = pa.pack_seqlens(q_lens)
+    got = pa.build_task_table(pa.make_params(hq, hkv, d, bs, **kw), cu, ctx, block_table=bt)
+    ref_t, ref_c, ref_np, _, ref_bal = ot.build_task_table(ot.Params(hq, hkv, d, bs, **kw), cu,
+                                                           ctx, bt)
+    assert np.array_equal(got.tasks, ref_t)
+    assert np.array_equal(got.combines, ref_c)
+    assert got.num_partials == ref_np
+    assert got.balance_snake == ref_bal["snake"]
+    assert got.balance_modulo == ref_bal["modulo"]
+    return got
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_shared_table_bit_exact_random(seed):
+    rng = np.random.default_rng(300 + seed)
+    bs = int(rng.choice([16, 32, 64]))
+    q, ctx, bt = aliased_batch(rng, bs, int(rng.integers(1, 9)))
+    hkv = int(rng.choice([1, 2, 4]))
+    got = compare_shared(q, ctx, bt, hq=hkv * int(rng.choice([1, 2, 4, 8, 16])), hkv=hkv, bs=bs,
+                         dec_split=64 * int(rng.integers(1, 4)), pf_q_tile=int(rng.integers(1, 9)),
+                         num_workers=int(rng.integers(1, 40)), decode_weight=int(rng.integers(1, 3)),
+                         verify_rows=int(rng.choice([0, 4])),
+                         shared_min=64 * int(rng.integers(0, 4)))
+    assert got.tasks.shape[0] > 0
+
+
+def test_shared_table_bit_exact_on_workload():
+    w = synth.make_workload("decode_shared_mha_bf16")
+    got = compare_shared(w.q_lens, w.ctx_lens, w.block_table, hq=32, hkv=32, bs=16,
+                         dec_split=1024, num_workers=512, shared_min=64)
+    kinds = set(got.tasks[:, 0].tolist())
+    assert kinds == {_abi.PA_TASK_DECODE, _abi.PA_TASK_SHARED}
+    # one shared pass per (group, kv head, piece): 8 groups of 16 members, one column set each
+    shared = got.tasks[got.tasks[:, 0] == _abi.PA_TASK_SHARED]
+    assert set(shared[:, 4].tolist()) == {16}
+    # the shared length is the prefix rounded down to a multiple of 64
+    assert len(shared) == 32 * sum(-(-(p // 64 * 64) // 1024) for p in w.extra["prefix_lens"])
+
+
+def test_shared_table_errors():
+    bt = np.array([[0, 1, 2, 3, 4, 5, 6, -1], [0, 1, 2, 3, 4, 7, 8, -1]], dtype=np.int32)
+    cu = np.array([0, 1, 2], np.int32)
+    ctx = np.array([100, 90], np.int32)
+    with pytest.raises(pa.PagedAttnError) as e:           # sharing needs the table
+        pa.build_task_table(pa.make_params(2, 1, 64, 16, shared_min=64), cu, ctx)
+    assert e.value.code == _abi.PA_ERR_INPUT
+    with pytest.raises(pa.PagedAttnError) as e:           # not a multiple of 64
+        pa.build_task_table(pa.make_params(2, 1, 64, 16, shared_min=32), cu, ctx, block_table=bt)
+    assert e.value.code == _abi.PA_ERR_SHAPE
+    with pytest.raises(pa.PagedAttnError) as e:           # a shared block receives a new row
+        pa.build_task_table(pa.make_params(2, 1, 64, 16, shared_min=64), cu,
+                            np.array([40, 48], np.int32), block_table=bt[:, :3].copy() * 0 +
+                            np.array([0, 1, 2], np.int32))
+    assert e.value.code == _abi.PA_ERR_INPUT
+    with pytest.raises(pa.PagedAttnError) as e:           # table narrower than a context needs
+        pa.build_task_table(pa.make_params(2, 1, 64, 16, shared_min=64), cu,
+                            np.array([100, 200], np.int32), block_table=bt)
+    assert e.value.code == _abi.PA_ERR_SHAPE
+    L = pa.lib()
+    nt, nc, npart = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    p = pa.make_params(2, 1, 64, 16, shared_min=64)
+    rc = L.build_task_table_shared(ctypes.byref(p), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, None, 8,
+                                   None, 0, ctypes.byref(nt), None, 0, ctypes.byref(nc),
+                                   ctypes.byref(npart), None)
+    assert rc == _abi.PA_ERR_NULL
+    # shared_min 0: the plain table, block table or not
+    plain = pa.build_task_table(pa.make_params(2, 1, 64, 16), cu, ctx)
+    off = pa.build_task_table(pa.make_params(2, 1, 64, 16), cu, ctx, block_table=bt)
+    assert np.array_equal(plain.tasks, off.tasks) and np.array_equal(plain.combines, off.combines)

@@ -1,0 +1,66 @@
+"""GPU parity for shared-prefix attention: decode sequences whose block tables alias their
+leading blocks run PA_TASK_SHARED tasks (the prefix read once for several sequences) plus their
+own decode splits, merged by the combine; outputs against the fp64 oracle, which reads every
+sequence's keys through its own table row. Run on an MI355X with the library built in-tree."""
+import numpy as np
+import pytest
+
+import synth
+from paged_variable_length_amd import _abi
+from tests.helpers import aliased_workload
+from tests.test_gpu_parity import _announce, small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _has_shared(plan):
+    return bool(np.any(plan.table.tasks[:, 0] == _abi.PA_TASK_SHARED))
+
+
+def _decode_groups(rng, n_groups, bs, hq, hkv, d, dtype="bf16", max_members=20):
+    prefix = rng.integers(1, 40, size=n_groups) * bs
+    own = [rng.integers(1, 300, size=int(rng.integers(1, max_members + 1)))
+           for _ in range(n_groups)]
+    return synth.shared_prefix_workload(prefix, own, hq, hkv, d, bs, dtype=dtype,
+                                        seed=int(rng.integers(1 << 30)), spare_blocks=3)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dec_split", [(8, 8, 128, 16, 64), (8, 4, 128, 16, 128),
+                                                   (16, 4, 64, 32, 64), (16, 2, 128, 64, 192),
+                                                   (32, 4, 128, 16, 64)])
+def test_shared_decode_small(hq, hkv, d, bs, dec_split):
+    rng = np.random.default_rng(hq * 100 + hkv * 10 + bs)
+    w = _decode_groups(rng, 5, bs, hq, hkv, d)
+    _announce(f"shared decode groups={w.extra['prefix_lens']}")
+    (mx, _), out, _, plan = small_case(w, "decode", dec_split=dec_split, shared_min=64)
+    assert _has_shared(plan)
+
+
+def test_shared_decode_fp32():
+    rng = np.random.default_rng(5)
+    w = _decode_groups(rng, 3, 16, 4, 2, 64, dtype="fp32", max_members=9)
+    _, _, _, plan = small_case(w, "decode", dec_split=64, shared_min=64)
+    assert _has_shared(plan)
+
+
+@pytest.mark.parametrize("seed,G", [(1, 1), (2, 2), (3, 4), (4, 8)])
+def test_shared_in_mixed_launch(seed, G):
+    """Groups between prefill and verify sequences, through the unified launch."""
+    rng = np.random.default_rng(40 + seed)
+    w = aliased_workload(rng, 16, 8, 2 * G, 2, 128, seed=seed)
+    (mx, _), out, _, plan = small_case(w, "varlen", dec_split=64, pf_q_tile=64, verify_rows=4,
+                                       shared_min=64)
+    assert _has_shared(plan)
+
+
+def test_shared_decode_full_size_sampled():
+    """The 128-request agent batch (8 prompts x 16 requests) in the benchmark's tiling; a seeded
+    sample of requests from every group against the oracle."""
+    w = synth.make_workload("decode_shared_mha_bf16")
+    rng = np.random.default_rng(9)
+    seqs = sorted(set((16 * np.arange(8) + rng.integers(0, 16, size=8)).tolist() + [0, 127]))
+    _announce(f"shared decode full N={w.num_seqs} sampled {seqs}")
+    _, out, _, plan = small_case(w, "decode", seqs=seqs, dec_split=1024, shared_min=64)
+    assert _has_shared(plan)
+    import torch
+    assert torch.isfinite(out).all()

@@ -8,7 +8,7 @@ import synth
 from oracle import attention as oa
 from oracle import cache as oc
 from oracle import task_table as ot
-from tests.helpers import to_np
+from tests.helpers import aliased_batch, to_np
 
 
 # ---------------------------------------------------------------- reshape_and_cache
@@ -280,41 +280,12 @@ def test_shared_column_sets_are_balanced():
         assert [f for f, _ in got] == list(np.cumsum([0] + sizes[:-1]))
 
 
-def _aliased_batch(rng, bs, n_groups, G):
-    """Decode sequences in runs that share a random number of leading blocks, a prefill and a
-    verify sequence in between, and private blocks for everything else."""
-    rows, ctx, q = [], [], []
-    nxt = 1000
-    for g in range(n_groups):
-        shared = [nxt + i for i in range(int(rng.integers(0, 17)))]
-        nxt += len(shared)
-        for m in range(int(rng.integers(1, 6))):
-            c = len(shared) * bs + int(rng.integers(1, 200))
-            need = -(-c // bs)
-            row = shared + list(range(nxt, nxt + need - len(shared)))
-            nxt += need - len(shared)
-            rows.append(row)
-            ctx.append(c)
-            q.append(1)
-        if g % 2:
-            c = int(rng.integers(5, 90))
-            rows.append(list(range(nxt, nxt + -(-c // bs))))
-            nxt += -(-c // bs)
-            ctx.append(c)
-            q.append(int(rng.integers(2, 5)))
-    width = max(len(r) for r in rows)
-    bt = np.full((len(rows), width), -1, dtype=np.int64)
-    for i, r in enumerate(rows):
-        bt[i, :len(r)] = r
-    return q, ctx, bt
-
-
 @pytest.mark.parametrize("seed,G,bs,dec_split,shared_min",
                          [(1, 1, 16, 64, 64), (2, 2, 16, 128, 64), (3, 4, 32, 64, 128),
                           (4, 8, 64, 64, 64), (5, 1, 16, 64, 192)])
 def test_shared_coverage_and_partials(seed, G, bs, dec_split, shared_min):
     rng = np.random.default_rng(seed)
-    q_lens, ctx, bt = _aliased_batch(rng, bs, 8, G)
+    q_lens, ctx, bt = aliased_batch(rng, bs, 8)
     cu = oa.pack_lengths(q_lens).tolist()
     hkv = 2
     p = P(num_q_heads=hkv * G, num_kv_heads=hkv, block_size=bs, dec_split=dec_split,
@@ -362,7 +333,7 @@ def test_planted_shared_length_mistake_is_caught(monkeypatch):
     """An oracle whose pairwise shared length runs one 64-key step past the aliased blocks
     must fail the aliasing pin."""
     rng = np.random.default_rng(1)
-    q_lens, ctx, bt = _aliased_batch(rng, 16, 8, 1)
+    q_lens, ctx, bt = aliased_batch(rng, 16, 8)
     cu = oa.pack_lengths(q_lens).tolist()
     p = P(num_q_heads=2, num_kv_heads=2, block_size=16, dec_split=64, pf_q_tile=3,
           verify_rows=4, shared_min=64, num_workers=5)
