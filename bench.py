@@ -55,7 +55,7 @@ TILING = {
     "decode_mha_fp8": dict(dec_split=1024),
     # 8 prompts x 16 decoding requests that alias the prompt's blocks: the prefix is read once
     # per group and kv head; the variant runs the same batch without grouping
-    "decode_shared_mha_bf16": dict(dec_split=1024, shared_min=64),
+    "decode_shared_mha_bf16": dict(dec_split=4096, shared_min=64),
     "decode_shared_mha_bf16:no_sharing": dict(dec_split=1024),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
