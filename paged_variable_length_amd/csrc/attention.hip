@@ -886,29 +886,53 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
 
   // ---- the three pieces of work on a tile. The loop runs them software-pipelined: the
   // scores of tile j+1 are computed while the exponentials of tile j are formed, and the
-  // value product of tile j runs while the maximum of tile j+1 is taken, so the matrix cores
-  // and the vector ALUs work on independent data inside one wave. Each matrix instruction is
-  // followed by its share of the vector work, and sched_barrier keeps that order: the
-  // scheduler would otherwise gather all exponentials in one place.
+  // value product of tile j runs while the causal mask of tile j+1 is applied, so the matrix
+  // cores and the vector ALUs work on independent data inside one wave. Each matrix
+  // instruction is followed by its share of the vector work, and sched_barrier keeps that
+  // order: the scheduler would otherwise gather all exponentials in one place.
+  //
+  // Reference maximum. The exponentials of a tile are taken against the running reference m
+  // without first taking the tile's maximum: only the wave's first tile sets m from its exact
+  // maximum. Each lane sums its tile's weights (the bf16-rounded values the value product
+  // uses, so numerator and denominator use the same weights); a sum above 2^16 (or an
+  // infinite one) bounds every weight of that lane only loosely, so the wave then takes the
+  // tile's true maximum, rescales acc and l to it and forms the exponentials again. Otherwise
+  // every weight is at most 2^16 and the result is the same softmax with another reference.
+  // Rows with a visible key in the first tile have l >= 1 from then on, so later tiles far
+  // below m only lose what fp32 would lose anyway.
   u32x4 pw[4];                              // P of the current tile, bf16, per PV k-step
-  // Phase A: scores of the next tile (K buffer KB) into sn; exponentials of sc into pw.
-  auto phase_a = [&](auto kb_tag, auto do_qk, auto do_exp, f32x16 (&sn)[2], f32x16 (&sc)[2]) {
+  // Phase A: scores of the next tile (K buffer KB) into sn; exponentials of sc into pw, their
+  // sum into psum.
+  auto phase_a = [&](auto kb_tag, auto do_qk, auto do_exp, f32x16 (&sn)[2], f32x16 (&sc)[2],
+                     float& psum) {
     constexpr int KOFF = decltype(kb_tag)::value * C::kTileBytes;
     constexpr bool QK = decltype(do_qk)::value, EXP = decltype(do_exp)::value;
     const float muse = m == -INFINITY ? 0.f : m;
-    float psum = 0.f;
-    // word w of pw (0..15): exponentials of scores 2w, 2w+1 of key block w / 8
+    float ps0 = 0.f, ps1 = 0.f;
+    float ep0 = 0.f, ep1 = 0.f;             // exponentials of the previous word
+    // packs the exponentials of word w (held in ep0, ep1) and adds them to a partial sum
+    auto pack_word = [&](int w) {
+      uint32_t word = pack_bf16x2(ep0, ep1);
+      // pins the word here: without it the packing sinks towards its first use in the value
+      // product, after the matrix steps it is meant to overlap
+      asm volatile("" : "+v"(word));
+      pw[w >> 2][w & 3] = word;
+      const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+      if (w & 1)
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), one2, ps1, false);
+      else
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), one2, ps0, false);
+    };
+    // word w of pw (0..15): exponentials of scores 2w, 2w+1 of key block w / 8. The previous
+    // word is packed after these exponentials are issued, so no packing waits on a
+    // transcendental result.
     auto exp_word = [&](int w) {
       const int kb = w >> 3, r = 2 * (w & 7);
       const float e0 = fast_exp2(fmaf(sc[kb][r], c, -muse));
       const float e1 = fast_exp2(fmaf(sc[kb][r + 1], c, -muse));
-      psum += e0;
-      psum += e1;
-      uint32_t word = pack_bf16x2(e0, e1);
-      // pins the word here: without it the exponentials sink towards their first use in
-      // the value product, after the matrix steps they are meant to overlap
-      asm volatile("" : "+v"(word));
-      pw[w >> 2][w & 3] = word;
+      if (w > 0) pack_word(w - 1);
+      ep0 = e0;
+      ep1 = e1;
     };
     if constexpr (QK) {
 #pragma unroll
@@ -964,10 +988,43 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         for (int w = 8; w < 16; ++w) exp_word(w);
       }
     }
-    if constexpr (EXP) l += psum;
+    if constexpr (EXP) {
+      pack_word(15);
+      psum = ps0 + ps1;
+    }
   };
-  // Phase B: value product of the current tile (V buffer VB) with pw, and mask and maximum
-  // of the next tile's scores sn (starting at key ts_next); then the lazy rescale.
+  // The slow path of the reference maximum: the true maximum of the scores sc of the current
+  // tile becomes the reference (when above m), acc and l are rescaled to it and the
+  // exponentials and their sum are formed again.
+  auto retake = [&](f32x16 (&sc)[2], float& psum) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
+    const float mnew = fmaxf(m, mx);
+    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] *= alpha;
+    m = mnew;
+    const float muse = m == -INFINITY ? 0.f : m;
+    float ps = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int kb = w >> 3, r = 2 * (w & 7);
+      const uint32_t word = pack_bf16x2(fast_exp2(fmaf(sc[kb][r], c, -muse)),
+                                        fast_exp2(fmaf(sc[kb][r + 1], c, -muse)));
+      pw[w >> 2][w & 3] = word;
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), ps, false);
+    }
+    psum = ps;
+  };
+  // Phase B: value product of the current tile (V buffer VB) with pw, and the causal mask of
+  // the next tile's scores sn (starting at key ts_next); with MAX also the maximum of sn and
+  // the rescale to it (the wave's first tile only).
   auto phase_b = [&](auto vb_tag, auto do_pv, auto do_max, f32x16 (&sn)[2], int ts_next) {
     constexpr int VOFF = decltype(vb_tag)::value * C::kTileBytes;
     constexpr bool PV = decltype(do_pv)::value, MAX = decltype(do_max)::value;
@@ -981,14 +1038,12 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         ds_read_b64_tr_b16_x4_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
     };
     float mx = -INFINITY;
-    if constexpr (MAX) {
-      if (ts_next + C::kTile - 1 > wave_pos_lo || ts_next + C::kTile > kv1) {
-        // score (kb, r) holds key ts_next + 4*g2 + off with off = 32kb + 8(r/4) + r%4; it is
-        // visible iff key < min(kv1, pos + 1), i.e. off < lim
-        const int lim = min(kv1, prefix + qi + 1) - ts_next - 4 * g2;
-        mask_block<0>(sn[0], lim);
-        mask_block<32>(sn[1], lim);
-      }
+    if (ts_next + C::kTile - 1 > wave_pos_lo || ts_next + C::kTile > kv1) {
+      // score (kb, r) holds key ts_next + 4*g2 + off with off = 32kb + 8(r/4) + r%4; it is
+      // visible iff key < min(kv1, pos + 1), i.e. off < lim
+      const int lim = min(kv1, prefix + qi + 1) - ts_next - 4 * g2;
+      mask_block<0>(sn[0], lim);
+      mask_block<32>(sn[1], lim);
     }
     // k-step kk: NB matrix steps, each followed by the maximum over a share of sn
     constexpr int kMaxPer = 32 / (4 * NB);  // scores folded per matrix step
@@ -1029,18 +1084,8 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     if constexpr (PV) lds_wait<0>(vr1);
     pv(3, vr1);
     if constexpr (MAX) {
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
-      // Lazy rescale: keep the running max while the tile's max exceeds it by at most 8
-      // (weights stay <= 2^8); numerator and denominator share the same reference, so the
-      // result is unchanged.
-      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int n = 0; n < NB; ++n) acc[n] *= alpha;
-        m = mnew;
-      }
+      // the first tile: its exact maximum becomes the reference (acc and l are still zero)
+      m = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -1062,13 +1107,14 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (nw > 0) {
-    phase_a(I0(), T_(), F_(), sa, sb);
+    float unused;
+    phase_a(I0(), T_(), F_(), sa, sb, unused);
     phase_b(I0(), F_(), T_(), sa, kv0);
   }
 
   // ---- iteration j: wait for K(j+1) and V(j); load K(j+2) and V(j+1) into the buffers the
   // previous iteration finished with; exponentials of j with scores of j+1; value product
-  // of j with mask and maximum of j+1. Unrolled by two so buffers and score sets are named
+  // of j with the mask of j+1. Unrolled by two so buffers and score sets are named
   // statically: even j reads K buffer 1, V buffer 0, keeps scores of j in sa.
   auto iteration = [&](int j, auto par_tag, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
     constexpr int PAR = decltype(par_tag)::value;
@@ -1086,11 +1132,14 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     idN = block_id(j + 4);
     // The scores of tile j+1 are formed even when this wave has no key to see there (its
     // last tile, or past the range): the mask then sets all of them to -inf, whatever the K
-    // buffer holds, and the maximum leaves the running state unchanged. One code path keeps
-    // the accumulators in place across the loop.
+    // buffer holds, and their weights are zero. One code path keeps the accumulators in
+    // place across the loop.
     if (j < nw) {
-      phase_a(std::integral_constant<int, 1 - PAR>(), T_(), T_(), snext, scur);
-      phase_b(std::integral_constant<int, PAR>(), T_(), T_(), snext, kv0 + (j + 1) * C::kTile);
+      float psum;
+      phase_a(std::integral_constant<int, 1 - PAR>(), T_(), T_(), snext, scur, psum);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 65536.f)) != 0) retake(scur, psum);
+      l += psum;
+      phase_b(std::integral_constant<int, PAR>(), T_(), F_(), snext, kv0 + (j + 1) * C::kTile);
     }
   };
   for (int j = 0; j < ntiles; j += 2) {

@@ -199,6 +199,24 @@ def test_prefill_ragged(d, tiling):
     small_case(w, "varlen", dec_split=64, **tiling)
 
 
+@pytest.mark.parametrize("q_mult", [8.0, 32.0])
+def test_prefill_scores_far_above_the_first_tile(q_mult):
+    """Queries scaled by a power of two (exact in bf16) spread the scores so widely that later
+    key tiles often hold scores far above everything in a wave's first tile: the prefill tile
+    loop then has to move its reference maximum (weights above 2^16 otherwise), which N(0,1)
+    inputs never make it do."""
+    q = [64, 200, 300, 129]
+    ctx = [64 + 500, 200, 300 + 77, 129 + 1000]
+    w = synth.custom_workload(q, ctx, 8, 2, 128, 16, seed=int(q_mult), spare_blocks=2)
+    _announce(f"prefill q x {q_mult} N={w.num_seqs} T={w.num_tokens}")
+    vals = {k: v.to(DEV) for k, v in synth.make_values(w, device="cpu").items()}
+    vals["q"] = (vals["q"].float() * q_mult).to(vals["q"].dtype)
+    h = host_subset(w, vals, list(range(w.num_seqs)))
+    out, _ = run_gpu(w, vals, "varlen", dec_split=64, pf_q_tile=128, pf_kv_split=0)
+    ref = oracle_subset(h, 1.0 / math.sqrt(w.head_dim))
+    check_close(to_np(out)[h["rows"]], ref, "bf16", f"q x {q_mult}")
+
+
 @pytest.mark.parametrize("bs", [16, 64, 256])
 def test_mixed_decode_and_chunks(bs):
     q = [1, 512, 1, 1, 77, 1, 200]
