@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 enum pa_status {
   PA_OK = 0,
@@ -295,6 +295,69 @@ int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_page
 int pa_validate_block_table(const int32_t* block_table_host, int32_t max_blocks_per_seq,
                             const int32_t* context_lens_host, int32_t num_seqs,
                             int32_t num_blocks, int32_t block_size);
+
+/* ---- SmoothGEMM: the Linear-layer product of the same step (XY-Serve page, section 2.2,
+ * "SmoothGEMM": a product of arbitrary M, N, K computed in fixed blocks that load and store
+ * only valid data, with no padded copies in memory; section 4.4, decompose_linear: output
+ * blocks times reduction blocks, each recording its actual shape and a load of
+ * actual_m * actual_n * actual_k, sorted by load like the attention tasks).
+ *   C = A W^T: A bf16 [M, K], W bf16 [N, K] (a Linear weight; both contiguous along K),
+ *   C bf16 [M, N], all row-major; fp32 accumulation; C rounded to nearest even.
+ *
+ * One task (8 x int32): output rows [m0, m0 + rows), columns [n0, n0 + cols), reduction
+ * indices [k0, k1). slot -1: the task covers all of K and writes C; slot >= 0: it writes fp32
+ * partial tile `slot` of the workspace, merged into C by a reduce record. */
+typedef struct pa_gemm_task {
+  int32_t m0, rows, n0, cols, k0, k1, slot, reserved;
+} pa_gemm_task;
+
+/* One merge (8 x int32): C[m0 .. m0+rows, n0 .. n0+cols) = sum of partial tiles first_slot ..
+ * first_slot + n_slots - 1, rounded to bf16. */
+typedef struct pa_gemm_reduce {
+  int32_t m0, rows, n0, cols, first_slot, n_slots, reserved0, reserved1;
+} pa_gemm_reduce;
+
+/* Decomposition parameters.
+ *   tile        output block edge, 128 or 256 (square blocks; the last row and column blocks
+ *               hold what is left)
+ *   k_split     0: one task covers all of K; else a positive multiple of 64, the reduction
+ *               length of one task (the page chains the K blocks of one output block by a
+ *               dependency; here they are independent tasks whose partial tiles are summed)
+ *   num_workers workers assumed by the balance report
+ *   reserved    must be 0 */
+typedef struct pa_gemm_params {
+  int32_t tile, k_split, num_workers, reserved;
+} pa_gemm_params;
+
+/* The Linear decomposition (XY-Serve page, section 4.4, decompose_linear), on the host:
+ * emission order row block, column block, K block; loads rows*cols*(k1-k0) (int64); tasks
+ * stably sorted by load, descending. Partial slots are numbered in emission order, one per task
+ * of an output block with more than one K piece, and each such block gets one reduce record
+ * (emission order). Capacity and balance conventions as build_task_table.
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (tile, k_split, num_workers, reserved, negative sizes,
+ *   K = 0 with M, N > 0), PA_ERR_CAPACITY. M = 0 or N = 0 gives an empty table. Pure, no HIP
+ *   calls. */
+int build_gemm_table(const pa_gemm_params* params, int32_t M, int32_t N, int32_t K,
+                     pa_gemm_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                     pa_gemm_reduce* reduces, int32_t reduces_cap, int32_t* num_reduces,
+                     int32_t* num_slots, double* balance);
+
+/* Workspace bytes for num_slots fp32 partial tiles of tile x tile, rounded up to 256 bytes;
+ * 0 when num_slots <= 0 or the tile is not 128 or 256. */
+size_t pa_gemm_workspace_bytes(int32_t num_slots, int32_t tile);
+
+/* Run a table from build_gemm_table (same M, N, K and tile; tasks_dev [num_tasks] and
+ * reduces_dev [num_reduces] copied to the device by the caller), then its reduces, on `stream`.
+ * Device pointers a, w, c (and workspace when num_reduces > 0: at least
+ * pa_gemm_workspace_bytes(num_slots, tile) bytes). When K is a multiple of 8 and a, w are
+ * 16-byte aligned, stages load through direct global->LDS loads; otherwise element by element
+ * (same results, slower). Elements of C outside the tasks' blocks are not written.
+ *   Errors: PA_ERR_SHAPE (negative sizes or counts, tile, tasks for an empty product),
+ *   PA_ERR_NULL, PA_ERR_CAPACITY (workspace), PA_ERR_HIP. num_tasks == 0 is a no-op. */
+int smooth_gemm(const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
+                int32_t tile, const pa_gemm_task* tasks_dev, int32_t num_tasks,
+                const pa_gemm_reduce* reduces_dev, int32_t num_reduces, int32_t num_slots,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

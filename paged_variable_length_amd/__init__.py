@@ -13,6 +13,10 @@ falls back to a CPU path: a missing library raises.
     paged_attn_varlen_prefill  packed causal attention, any mix of decode and prefill (device)
     validate_block_table     debug check of a host block table
     StepPlan                 convenience: a built table copied to the device with its workspace
+    build_gemm_table         SmoothGEMM's Linear decomposition: load-sorted tile tasks (host)
+    gemm_workspace_bytes     bytes of SmoothGEMM's partial tiles
+    smooth_gemm              C = A W^T for arbitrary M, N, K from a task table (device)
+    GemmPlan                 convenience: a built SmoothGEMM table on the device
 """
 from __future__ import annotations
 
@@ -23,12 +27,14 @@ import numpy as np
 
 from . import _abi
 from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F401
-                   PA_TASK_VERIFY, PagedAttnError, PaCombine, PaParams, PaTask, check, lib)
+                   PA_TASK_VERIFY, PagedAttnError, PaCombine, PaGemmParams, PaGemmReduce,
+                   PaGemmTask, PaParams, PaTask, check, lib)
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
            "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
            "reshape_and_cache_fp8", "paged_attn_decode_fp8",
-           "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32"]
+           "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32",
+           "build_gemm_table", "gemm_workspace_bytes", "smooth_gemm", "GemmTable", "GemmPlan"]
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -358,3 +364,84 @@ class StepPlan:
         paged_attn_varlen_prefill(q, k_pages, v_pages, self.block_table, self.cu, self.ctx,
                                   scale, self.tasks, self.combines, self.num_partials,
                                   self.workspace, out, stream)
+
+
+# ------------------------------------------------------------------ SmoothGEMM
+@dataclass
+class GemmTable:
+    tasks: np.ndarray        # int32 [n, 8]: m0, rows, n0, cols, k0, k1, slot, 0
+    reduces: np.ndarray      # int32 [m, 8]: m0, rows, n0, cols, first_slot, n_slots, 0, 0
+    num_slots: int
+    balance_snake: float
+    balance_modulo: float
+
+
+def build_gemm_table(M, N, K, tile=256, k_split=0, num_workers=256) -> GemmTable:
+    """Host Linear decomposition for C = A W^T (library call; sized by a first call)."""
+    L = lib()
+    prm = PaGemmParams(int(tile), int(k_split), int(num_workers), 0)
+    nt, nr, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = L.build_gemm_table(ctypes.byref(prm), int(M), int(N), int(K), None, 0, ctypes.byref(nt),
+                            None, 0, ctypes.byref(nr), ctypes.byref(ns), None)
+    if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
+        check(rc, "build_gemm_table")
+    tasks = np.zeros((nt.value, 8), dtype=np.int32)
+    reds = np.zeros((nr.value, 8), dtype=np.int32)
+    bal = (ctypes.c_double * 2)()
+    rc = L.build_gemm_table(ctypes.byref(prm), int(M), int(N), int(K),
+                            tasks.ctypes.data_as(ctypes.POINTER(PaGemmTask)), tasks.shape[0],
+                            ctypes.byref(nt), reds.ctypes.data_as(ctypes.POINTER(PaGemmReduce)),
+                            reds.shape[0], ctypes.byref(nr), ctypes.byref(ns), bal)
+    check(rc, "build_gemm_table")
+    return GemmTable(tasks, reds, ns.value, bal[0], bal[1])
+
+
+def gemm_workspace_bytes(num_slots: int, tile: int) -> int:
+    return int(lib().pa_gemm_workspace_bytes(int(num_slots), int(tile)))
+
+
+def smooth_gemm(a, w, c, tile, tasks_dev, reduces_dev, num_slots, workspace, stream=None):
+    """C [M, N] = A [M, K] W [N, K]^T in bf16 with fp32 accumulation (library kernels), from a
+    table built by build_gemm_table for the same M, N, K and tile, copied to the device."""
+    torch = _torch()
+    if a.dim() != 2 or w.dim() != 2 or c.dim() != 2:
+        raise ValueError("a, w, c must be 2-D")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(c.shape) != (M, N):
+        raise ValueError(f"shapes disagree: a {tuple(a.shape)}, w {tuple(w.shape)}, "
+                         f"c {tuple(c.shape)}")
+    args = [_dev(a, "a", torch.bfloat16), _dev(w, "w", torch.bfloat16),
+            _dev(c, "c", torch.bfloat16), M, N, K, int(tile),
+            _dev(tasks_dev, "tasks_dev", torch.int32, 2) if tasks_dev.numel() else None,
+            tasks_dev.shape[0]]
+    if reduces_dev.shape[0] > 0:
+        args += [_dev(reduces_dev, "reduces_dev", torch.int32, 2), reduces_dev.shape[0]]
+    else:
+        args += [None, 0]
+    ws, wsb = None, 0
+    if workspace is not None and workspace.numel() > 0:
+        ws = _dev(workspace, "workspace")
+        wsb = workspace.numel() * workspace.element_size()
+    args += [int(num_slots), ws, wsb, _stream(stream)]
+    check(lib().smooth_gemm(*args), "smooth_gemm")
+
+
+class GemmPlan:
+    """A SmoothGEMM table for one (M, N, K) built on the host and copied to the device, with
+    its workspace (torch allocations)."""
+
+    def __init__(self, M, N, K, tile=256, k_split=0, num_workers=256, device="cuda"):
+        torch = _torch()
+        self.M, self.N, self.K, self.tile = int(M), int(N), int(K), int(tile)
+        self.table = build_gemm_table(M, N, K, tile, k_split, num_workers)
+        self.tasks = torch.from_numpy(self.table.tasks).to(device)
+        self.reduces = torch.from_numpy(self.table.reduces).to(device)
+        nbytes = gemm_workspace_bytes(self.table.num_slots, tile)
+        self.workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
+
+    def run(self, a, w, c, stream=None):
+        if (a.shape[0], w.shape[0], a.shape[1]) != (self.M, self.N, self.K):
+            raise ValueError("operands do not match the plan's M, N, K")
+        smooth_gemm(a, w, c, self.tile, self.tasks, self.reduces, self.table.num_slots,
+                    self.workspace, stream)

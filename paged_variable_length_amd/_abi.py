@@ -25,7 +25,7 @@ PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -38,7 +38,8 @@ EXPORTS = ("pa_abi_version", "pa_last_error", "pa_pack_seqlens", "build_task_tab
            "pa_workspace_bytes", "reshape_and_cache", "paged_attn_decode",
            "paged_attn_varlen_prefill", "pa_validate_block_table", "reshape_and_cache_fp8",
            "paged_attn_decode_fp8",
-           "build_task_table_shared")
+           "build_task_table_shared", "build_gemm_table", "pa_gemm_workspace_bytes",
+           "smooth_gemm")
 
 
 class PaTask(ctypes.Structure):
@@ -49,6 +50,20 @@ class PaTask(ctypes.Structure):
 class PaCombine(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("seq", "q_row0", "q_rows", "head", "heads", "first_slot", "n_slots", "reserved")]
+
+
+class PaGemmTask(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("m0", "rows", "n0", "cols", "k0", "k1", "slot", "reserved")]
+
+
+class PaGemmReduce(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("m0", "rows", "n0", "cols", "first_slot", "n_slots", "reserved0", "reserved1")]
+
+
+class PaGemmParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("tile", "k_split", "num_workers", "reserved")]
 
 
 class PaParams(ctypes.Structure):
@@ -116,6 +131,16 @@ def lib() -> ctypes.CDLL:
                                         p, p]
     L.pa_validate_block_table.restype = ctypes.c_int
     L.pa_validate_block_table.argtypes = [pi32, i32, pi32, i32, i32, i32]
+    L.build_gemm_table.restype = ctypes.c_int
+    L.build_gemm_table.argtypes = [ctypes.POINTER(PaGemmParams), i32, i32, i32,
+                                   ctypes.POINTER(PaGemmTask), i32, pi32,
+                                   ctypes.POINTER(PaGemmReduce), i32, pi32, pi32,
+                                   ctypes.POINTER(ctypes.c_double)]
+    L.pa_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.pa_gemm_workspace_bytes.argtypes = [i32, i32]
+    L.smooth_gemm.restype = ctypes.c_int
+    L.smooth_gemm.argtypes = [p, p, p, i32, i32, i32, i32, p, i32, p, i32, i32, p,
+                              ctypes.c_size_t, p]
     if L.pa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libpagedattn ABI {L.pa_abi_version()} != binding {ABI_VERSION}")
     _lib = L

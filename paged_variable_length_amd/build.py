@@ -38,15 +38,19 @@ def build(verbose: bool = True) -> str:
     os.makedirs(out_dir, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
     host_o = os.path.join(out_dir, "host.o")
-    dev_o = os.path.join(out_dir, "attention.o")
     _run(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-c",
           os.path.join(CSRC, "host.cpp"), "-o", host_o] + inc)
-    # packed-fp32 instructions are disabled for all device code
-    _run([_hipcc(), f"--offload-arch={ARCH}", "-std=c++17", "-O3", "-fPIC", "-c",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          os.path.join(CSRC, "attention.hip"), "-o", dev_o] + inc)
+    dev_objs = []
+    for name in ("attention", "gemm"):
+        obj = os.path.join(out_dir, name + ".o")
+        # packed-fp32 instructions are disabled for all device code
+        _run([_hipcc(), f"--offload-arch={ARCH}", "-std=c++17", "-O3", "-fPIC", "-c",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              os.path.join(CSRC, name + ".hip"), "-o", obj] + inc)
+        dev_objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", host_o, dev_o, "-o", tmp])
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", host_o] + dev_objs +
+         ["-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

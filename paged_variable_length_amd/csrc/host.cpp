@@ -513,3 +513,79 @@ extern "C" int pa_validate_block_table(const int32_t* bt, int32_t width, const i
   }
   return pa::clear_error();
 }
+
+// Linear decomposition for SmoothGEMM (XY-Serve page, section 4.4, decompose_linear; section
+// 2.2, SmoothGEMM): output blocks of tile x tile, K pieces of k_split, loads of
+// rows * cols * k, stable sort by load, descending.
+extern "C" int build_gemm_table(const pa_gemm_params* p, int32_t M, int32_t N, int32_t K,
+                                pa_gemm_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
+                                pa_gemm_reduce* reduces, int32_t reduces_cap,
+                                int32_t* num_reduces, int32_t* num_slots, double* balance) {
+  if (!p || !num_tasks || !num_reduces || !num_slots)
+    return set_error(PA_ERR_NULL, "build_gemm_table: NULL pointer");
+  if (p->tile != 128 && p->tile != 256)
+    return set_error(PA_ERR_SHAPE, "tile %d must be 128 or 256", p->tile);
+  if (p->k_split < 0 || p->k_split % pa::kSplitQuantum)
+    return set_error(PA_ERR_SHAPE, "k_split %d must be 0 or a positive multiple of %d",
+                     p->k_split, pa::kSplitQuantum);
+  if (p->num_workers < 1) return set_error(PA_ERR_SHAPE, "num_workers must be >= 1");
+  if (p->reserved != 0) return set_error(PA_ERR_SHAPE, "pa_gemm_params.reserved must be zero");
+  if (M < 0 || N < 0 || K < 0) return set_error(PA_ERR_SHAPE, "negative size");
+  if (K == 0 && M > 0 && N > 0)
+    return set_error(PA_ERR_SHAPE, "K must be >= 1 for a non-empty product");
+  const int64_t tile = p->tile;
+  const int64_t split = p->k_split > 0 ? p->k_split : std::max<int64_t>(K, 1);
+  const int64_t mb = (M + tile - 1) / tile, nb = (N + tile - 1) / tile;
+  const int64_t nk = (K > 0 && M > 0 && N > 0) ? (K + split - 1) / split : 0;
+  const int64_t nt = mb * nb * nk, nr = nk > 1 ? mb * nb : 0, ns = nk > 1 ? nt : 0;
+  if (nt > INT32_MAX) return set_error(PA_ERR_SHAPE, "too many tasks");
+  *num_tasks = static_cast<int32_t>(nt);
+  *num_reduces = static_cast<int32_t>(nr);
+  *num_slots = static_cast<int32_t>(ns);
+  if (nt > tasks_cap || nr > reduces_cap)
+    return set_error(PA_ERR_CAPACITY, "build_gemm_table: need %lld tasks and %lld reduces",
+                     static_cast<long long>(nt), static_cast<long long>(nr));
+  if ((nt > 0 && !tasks) || (nr > 0 && !reduces))
+    return set_error(PA_ERR_NULL, "build_gemm_table: NULL output buffer");
+  std::vector<pa_gemm_task> emitted;
+  std::vector<int64_t> load;
+  emitted.reserve(static_cast<size_t>(nt));
+  load.reserve(static_cast<size_t>(nt));
+  int32_t slot = 0, r = 0;
+  for (int64_t m0 = 0; m0 < M && nk > 0; m0 += tile) {
+    const int32_t rows = static_cast<int32_t>(std::min<int64_t>(tile, M - m0));
+    for (int64_t n0 = 0; n0 < N; n0 += tile) {
+      const int32_t cols = static_cast<int32_t>(std::min<int64_t>(tile, N - n0));
+      const int32_t first = nk > 1 ? slot : -1;
+      if (nk > 1) {
+        reduces[r++] = pa_gemm_reduce{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
+                                      cols, first, static_cast<int32_t>(nk), 0, 0};
+        slot += static_cast<int32_t>(nk);
+      }
+      for (int64_t j = 0; j < nk; ++j) {
+        const int64_t k0 = j * split, k1 = std::min<int64_t>(K, k0 + split);
+        emitted.push_back(pa_gemm_task{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
+                                       cols, static_cast<int32_t>(k0), static_cast<int32_t>(k1),
+                                       nk > 1 ? first + static_cast<int32_t>(j) : -1, 0});
+        load.push_back(int64_t(rows) * cols * (k1 - k0));
+      }
+    }
+  }
+  std::vector<uint32_t> order(emitted.size());
+  std::iota(order.begin(), order.end(), 0u);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](uint32_t x, uint32_t y) { return load[x] > load[y]; });
+  for (size_t i = 0; i < order.size(); ++i) tasks[i] = emitted[order[i]];
+  if (balance) {
+    const int64_t W = p->num_workers;
+    std::vector<int64_t> snake(static_cast<size_t>(W), 0), modulo(static_cast<size_t>(W), 0);
+    for (size_t i = 0; i < order.size(); ++i) {
+      const int64_t rnd = static_cast<int64_t>(i) / W, pos = static_cast<int64_t>(i) % W;
+      snake[static_cast<size_t>(rnd % 2 == 0 ? pos : W - 1 - pos)] += load[order[i]];
+      modulo[static_cast<size_t>(pos)] += load[order[i]];
+    }
+    balance[0] = ratio(snake);
+    balance[1] = ratio(modulo);
+  }
+  return pa::clear_error();
+}

@@ -23,7 +23,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_workload", "deal_block_table", "make_values",
-           "make_fp8_pages", "custom_workload", "shared_prefix_workload"]
+           "make_fp8_pages", "custom_workload", "shared_prefix_workload", "GEMM_SHAPES",
+           "gemm_shape", "make_gemm_operands"]
 
 
 @dataclass
@@ -289,3 +290,39 @@ def make_fp8_pages(w: Workload, device="cpu", seed: int | None = None, nan_senti
          for k, v in dict(k_codes=k_codes, v_codes=v_codes, k_scales=k_scales,
                           v_scales=v_scales).items()}
     return t
+
+
+# ---------------------------------------------------------------- Linear (SmoothGEMM) inputs
+# (M, N, K) of C = A W^T. The first three are the shapes of the XY-Serve page's Linear kernel
+# table (section 3.1); the others are Linear layers of this step's own batches: the query
+# projection over the packed prefill batch (M = its token count, which the seed decides; a
+# 32-head x 128 model of hidden size 4096) and the output projection over the mixed step
+# (M = 200 decode rows + 4 x 512 chunk rows; 64 heads x 128, hidden size 8192).
+GEMM_SHAPES = {
+    "linear_1024x1024x1024": (1024, 1024, 1024),
+    "linear_512x2048x1024": (512, 2048, 1024),
+    "linear_2048x512x2048": (2048, 512, 2048),
+    "linear_prefill_qproj": ("prefill_varlen_bf16", 4096, 4096),
+    "linear_mixed_oproj": ("mixed_bf16", 8192, 8192),
+}
+
+
+def gemm_shape(name: str):
+    """(M, N, K) of a named Linear shape; M of a batch-derived shape is its packed token
+    count."""
+    m, n, k = GEMM_SHAPES[name]
+    if isinstance(m, str):
+        w = make_workload(m)
+        m = int(w.q_lens.sum())
+    return int(m), int(n), int(k)
+
+
+def make_gemm_operands(M: int, N: int, K: int, device="cpu", seed: int = 0):
+    """A [M, K] and W [N, K]: N(0,1) drawn in fp32 with a seeded torch generator, rounded to
+    bf16."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    a = torch.randn(M, K, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return a, w
