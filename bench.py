@@ -37,7 +37,9 @@ METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
              "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8",
-             "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing"]
+             "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing",
+             "gemm_linear_prefill_qproj", "gemm_linear_mixed_oproj", "gemm_linear_1024x1024x1024",
+             "gemm_linear_512x2048x1024", "gemm_linear_2048x512x2048"]
 # Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
 # splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
 # query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
@@ -57,6 +59,17 @@ TILING = {
     # per group and kv head; the variant runs the same batch without grouping
     "decode_shared_mha_bf16": dict(dec_split=4096, shared_min=64),
     "decode_shared_mha_bf16:no_sharing": dict(dec_split=1024),
+}
+# SmoothGEMM (C = A W^T, bf16, fp32 accumulation) on Linear shapes: the pages' own Linear table
+# shapes and the q / o projections of this step's batches (synth.GEMM_SHAPES). Tile and K split
+# per shape from a sweep on MI355X: 256-wide tiles where there are enough of them to fill the
+# chip, 128-wide (and K pieces) where the product is small.
+GEMM_TILING = {
+    "gemm_linear_prefill_qproj": dict(tile=256, k_split=0),
+    "gemm_linear_mixed_oproj": dict(tile=128, k_split=0),
+    "gemm_linear_1024x1024x1024": dict(tile=128, k_split=0),
+    "gemm_linear_512x2048x1024": dict(tile=128, k_split=0),
+    "gemm_linear_2048x512x2048": dict(tile=128, k_split=512),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
@@ -362,7 +375,75 @@ def cpu_baseline(name, budget_s=12.0):
                       f"fp64 NumPy cache scatter + attention, {spent:.1f} s"}
 
 
+def run_gemm(name, steps, warmup, flush):
+    """One SmoothGEMM workload: a step is the host Linear decomposition into a pinned buffer,
+    its copy to the device and the GEMM launch (plus the partial-tile reduce when K is split).
+    Launch time from HIP events on the launch stream with L2/MALL evicted (a 1 GiB read)
+    between launches; torch.matmul (hipBLASLt) on the same operands is timed the same way as
+    a reference point."""
+    import torch
+    import synth
+    import paged_variable_length_amd as pa
+    shape = name[len("gemm_"):]
+    M, N, K = synth.gemm_shape(shape)
+    tl = GEMM_TILING[name]
+    a, w = synth.make_gemm_operands(M, N, K, device="cuda", seed=1)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    plan = pa.GemmPlan(M, N, K, tile=tl["tile"], k_split=tl["k_split"], num_workers=256)
+    nt = len(plan.table.tasks)
+    pin = torch.zeros((max(nt, 1), 8), dtype=torch.int32, pin_memory=True)
+
+    def step():
+        t = pa.build_gemm_table(M, N, K, tl["tile"], tl["k_split"], 256)
+        pin.numpy()[:nt] = t.tasks
+        plan.tasks.copy_(pin[:nt], non_blocking=True)
+        plan.run(a, w, c)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for e0, e1 in evs:
+            flush.sum()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = [x.elapsed_time(y) for x, y in evs]
+        return float(np.mean(ms)), float(np.min(ms)), float(np.median(ms))
+
+    n = max(steps, 10)
+    avg, mn, med = timed(lambda: plan.run(a, w, c), n)
+    lib_avg, _, _ = timed(lambda: torch.matmul(a, w.t()), n)
+    flops = 2.0 * M * N * K
+    tf = flops / (avg * 1e-3) / 1e12
+    res = {"workload": name, "shape_mnk": [M, N, K], "tiling": tl, "tasks": nt,
+           "reduces": len(plan.table.reduces),
+           "balance_snake": round(plan.table.balance_snake, 4),
+           "balance_modulo": round(plan.table.balance_modulo, 4),
+           "ms_per_step": round(step_s * 1e3, 4), "launch_ms_avg": round(avg, 4),
+           "launch_ms_min": round(mn, 4), "launch_ms_median": round(med, 4),
+           "flops": flops, "tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "bytes_min": 2 * (M * K + N * K + M * N),
+           "finite": bool(torch.isfinite(c).all()),
+           "torch_matmul_ms_avg": round(lib_avg, 4),
+           "torch_matmul_tflops": round(flops / (lib_avg * 1e-3) / 1e12, 2)}
+    del a, w, c, plan
+    torch.cuda.empty_cache()
+    return res
+
+
 def run(name, steps, warmup, with_launch_timing=True, flush=None):
+    if name.startswith("gemm_"):
+        return run_gemm(name, steps, warmup, flush)
     r = Runner(name)
     step_s = r.timed_steps(steps, warmup)
     res = {"workload": name, "ms_per_step": round(step_s * 1e3, 4), "tasks": r.num_tasks,
@@ -425,6 +506,17 @@ def main():
         print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
 
     head = run(args.workload, args.steps, args.warmup, True, flush)
+    if args.workload.startswith("gemm_"):
+        # a SmoothGEMM workload on its own (for profiling): its result is the whole line
+        print(f"[bench] {args.workload}: {head['launch_ms_avg']} ms launch, {head['tflops']} "
+              f"TFLOP/s (torch.matmul {head['torch_matmul_tflops']})", file=sys.stderr,
+              flush=True)
+        print(json.dumps({"metric": "SmoothGEMM TFLOP/s", "value": head["tflops"],
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": args.workload}, "detail": head}), flush=True)
+        return
     print(f"[bench] {args.workload}: {head['ms_per_step']} ms/step, attention launch "
           f"{head['attn_launch_ms_avg']} ms", file=sys.stderr, flush=True)
     secondary = {}
@@ -433,6 +525,12 @@ def main():
             if name == args.workload:
                 continue
             res = run(name, args.steps, args.warmup, True, flush)
+            if name.startswith("gemm_"):
+                secondary[name] = res
+                print(f"[bench] {name}: {res['launch_ms_avg']} ms launch, {res['tflops']} "
+                      f"TFLOP/s ({res['mfma_frac']:.1%} of MFMA peak; torch.matmul "
+                      f"{res['torch_matmul_tflops']})", file=sys.stderr, flush=True)
+                continue
             wk = res["work"]
             t_launch = res["attn_launch_ms_avg"] * 1e-3
             res["attn_gbs"] = round(wk["bytes"] / t_launch / 1e9, 1)

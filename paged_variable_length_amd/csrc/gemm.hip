@@ -163,6 +163,8 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
       const int base_row = op == 0 ? m0 : n0;
       const int nrows = op == 0 ? rows : cols;
       char* tile = smem + (2 * op + buf) * kTileBytes;
+      // every row of the tile exists and the stage is a whole 64: no lane is switched off
+      const bool interior = nrows == TILE && ks + kBK <= k1;
 #pragma unroll
       for (int q = 0; q < kPieces; ++q) {
         const int r0 = 8 * (wave * kPieces + q);          // the piece's first tile row
@@ -170,12 +172,18 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
         char* dst = tile + (wave * kPieces + q) * 1024;
         const bool row_ok = r0 + lrow < nrows;
         if constexpr (ALIGNED) {
+          const uint16_t* piece = src + static_cast<size_t>(base_row + r0) * K + ks;
+          if (interior) {
+            __builtin_amdgcn_global_load_lds(piece + loff[q & 1],
+                                             (__attribute__((address_space(3))) void*)dst, 16,
+                                             0, 0);
+            continue;
+          }
           // K % 8 == 0 and k1 is K or a multiple of 64: a chunk lies wholly inside [k0, k1)
           // or wholly past it
           if (kc >= k1) {
             *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
           } else if (row_ok) {
-            const uint16_t* piece = src + static_cast<size_t>(base_row + r0) * K + ks;
             __builtin_amdgcn_global_load_lds(piece + loff[q & 1],
                                              (__attribute__((address_space(3))) void*)dst, 16,
                                              0, 0);
@@ -260,13 +268,19 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
     lds_wait<NOPS>(o0);
     mfmas(o0, 0, NBN);
     // stage s+1's loads landed (this wave's share) and every wave's k-step-3 operands arrived;
-    // after the barrier stage s's buffers are free
+    // after the barrier stage s's buffers are free. The scheduling fences keep the matrix
+    // steps of k-step 2 ahead of the wait (the matrix pipe works while the wave waits) and
+    // the loads of stage s+2 between the two halves of k-step 3.
+    __builtin_amdgcn_sched_barrier(0);
     lds_wait<0>(o1);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     mfmas(o1, 0, NBN / 2);
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 2 < nst) load_stage(s + 2, s & 1);
     if (s + 1 < nst) read_ops(nxt, 0, o0);
+    __builtin_amdgcn_sched_barrier(0);
     mfmas(o1, NBN / 2, NBN);
   }
 
