@@ -379,8 +379,8 @@ def run_gemm(name, steps, warmup, flush):
     """One SmoothGEMM workload: a step is the host Linear decomposition into a pinned buffer,
     its copy to the device and the GEMM launch (plus the partial-tile reduce when K is split).
     Launch time from HIP events on the launch stream with L2/MALL evicted (a 1 GiB read)
-    between launches; torch.matmul (hipBLASLt) on the same operands is timed the same way as
-    a reference point."""
+    between launches; torch.mm (hipBLASLt) on the same operands, warmed up, is timed the same
+    way as a reference point."""
     import torch
     import synth
     import paged_variable_length_amd as pa
@@ -422,7 +422,13 @@ def run_gemm(name, steps, warmup, flush):
 
     n = max(steps, 10)
     avg, mn, med = timed(lambda: plan.run(a, w, c), n)
-    lib_avg, _, _ = timed(lambda: torch.matmul(a, w.t()), n)
+    # the library's first call picks its kernel (about 0.2 s); warm it up, write into a
+    # preallocated output
+    cref = torch.empty_like(c)
+    for _ in range(3):
+        torch.mm(a, w.t(), out=cref)
+    lib_avg, _, _ = timed(lambda: torch.mm(a, w.t(), out=cref), n)
+    del cref
     flops = 2.0 * M * N * K
     tf = flops / (avg * 1e-3) / 1e12
     res = {"workload": name, "shape_mnk": [M, N, K], "tiling": tl, "tasks": nt,
