@@ -165,6 +165,27 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
       char* tile = smem + (2 * op + buf) * kTileBytes;
       // every row of the tile exists and the stage is a whole 64: no lane is switched off
       const bool interior = nrows == TILE && ks + kBK <= k1;
+      if constexpr (ALIGNED && C::kWaves == 8) {
+        if (interior) {
+          // waves 0-3 load the pieces of waves w and w+4 and waves 4-7 load nothing: waves w
+          // and w+4 share a SIMD, so one of them can wait on its loads while the other keeps
+          // the matrix pipe busy (measured: +8% over every wave loading its own pieces, and
+          // better than alternating the loading half by stage)
+          if (wave < 4) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+              for (int q = 0; q < kPieces; ++q) {
+                const int slot = (wave + 4 * half) * kPieces + q;
+                const uint16_t* piece = src + static_cast<size_t>(base_row + 8 * slot) * K + ks;
+                __builtin_amdgcn_global_load_lds(
+                    piece + loff[q & 1],
+                    (__attribute__((address_space(3))) void*)(tile + slot * 1024), 16, 0, 0);
+              }
+          }
+          continue;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < kPieces; ++q) {
         const int r0 = 8 * (wave * kPieces + q);          // the piece's first tile row
