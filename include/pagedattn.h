@@ -205,8 +205,9 @@ size_t pa_workspace_bytes(int32_t num_partials, int32_t head_dim);
  *   Device pointers: k_new, v_new, k_pages, v_pages, block_table, cu_seqlens_q, context_lens.
  *   num_tokens must equal cu_seqlens_q[num_seqs] (not checked on the device). Two tokens
  *   mapped to one slot is malformed input (undefined which write wins).
- *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_tokens/num_seqs < 0, Hkv < 1, D not 64/128),
- *   PA_ERR_BLOCK_SIZE, PA_ERR_DTYPE, PA_ERR_HIP. num_tokens == 0 is a no-op. */
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_tokens/num_seqs < 0, num_tokens > 8,388,607 (one
+ *   workgroup per token), Hkv < 1, D not 64/128), PA_ERR_BLOCK_SIZE, PA_ERR_DTYPE,
+ *   PA_ERR_HIP. num_tokens == 0 is a no-op. */
 int reshape_and_cache(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
@@ -219,11 +220,13 @@ int reshape_and_cache(const void* k_new, const void* v_new, void* k_pages, void*
  * num_seqs (copied to the device by the caller: tasks_dev [num_tasks], combines_dev
  * [num_combines]), then merges split partials with a log-sum-exp combine. Each KV page is read
  * once for all query heads of its kv head, and a shared prefix once for its group's members.
+ *   Device pointers: q, k_pages, v_pages, block_table, context_lens, tasks_dev, combines_dev,
+ *   workspace, out.
  *   workspace: device buffer of at least pa_workspace_bytes(num_partials, D) bytes
- *   (may be NULL when num_combines == 0).
- *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (Hq % Hkv, Hq/Hkv > 16, D), PA_ERR_BLOCK_SIZE,
- *   PA_ERR_DTYPE, PA_ERR_CAPACITY (workspace too small for the combines' partial rows),
- *   PA_ERR_HIP. */
+ *   (may be NULL when num_partials == 0 and num_combines == 0).
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (Hq % Hkv, Hq/Hkv > 16, D, num_tasks or num_combines
+ *   above 8,388,607: one workgroup each), PA_ERR_BLOCK_SIZE, PA_ERR_DTYPE, PA_ERR_CAPACITY
+ *   (workspace too small for the partial rows), PA_ERR_HIP. num_tasks == 0 is a no-op. */
 int paged_attn_decode(const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -352,7 +355,8 @@ size_t pa_gemm_workspace_bytes(int32_t num_slots, int32_t tile);
  * pa_gemm_workspace_bytes(num_slots, tile) bytes). When K is a multiple of 8 and a, w are
  * 16-byte aligned, stages load through direct global->LDS loads; otherwise element by element
  * (same results, slower). Elements of C outside the tasks' blocks are not written.
- *   Errors: PA_ERR_SHAPE (negative sizes or counts, tile, tasks for an empty product),
+ *   Errors: PA_ERR_SHAPE (negative sizes or counts, tile, tasks for an empty product, more
+ *   than 8,388,607 workgroups in a launch: num_tasks, or num_reduces x tile^2 / 1024),
  *   PA_ERR_NULL, PA_ERR_CAPACITY (workspace), PA_ERR_HIP. num_tasks == 0 is a no-op. */
 int smooth_gemm(const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
                 int32_t tile, const pa_gemm_task* tasks_dev, int32_t num_tasks,

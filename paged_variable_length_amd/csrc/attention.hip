@@ -1411,6 +1411,9 @@ int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hk
                        int32_t num_partials, size_t ws_bytes, const void* ws, int32_t max_blocks) {
   if (num_seqs < 0 || num_tasks < 0 || num_combines < 0 || num_partials < 0 || max_blocks < 0)
     return pa::set_error(PA_ERR_SHAPE, "%s: negative size", who);
+  if (num_tasks > pa::kMaxWorkgroups || num_combines > pa::kMaxWorkgroups)
+    return pa::set_error(PA_ERR_SHAPE, "%s: %d tasks, %d combines: one launch takes at most %d",
+                         who, num_tasks, num_combines, pa::kMaxWorkgroups);
   if (hq < 1 || hkv < 1 || hq % hkv)
     return pa::set_error(PA_ERR_SHAPE, "%s: Hq %d is not a positive multiple of Hkv %d", who, hq, hkv);
   if (hq / hkv > pa::kMaxGroup)
@@ -1419,7 +1422,7 @@ int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hk
   if (!pa::block_size_ok(bs))
     return pa::set_error(PA_ERR_BLOCK_SIZE, "%s: block_size %d is not a power of two in [16, 256]", who, bs);
   if (dtype != PA_BF16 && dtype != PA_FP32) return pa::set_error(PA_ERR_DTYPE, "%s: dtype %d", who, dtype);
-  if (num_combines > 0) {
+  if (num_partials > 0 || num_combines > 0) {
     if (!ws) return pa::set_error(PA_ERR_NULL, "%s: workspace is NULL", who);
     const size_t need = pa_workspace_bytes(num_partials, d);
     if (ws_bytes < need)
@@ -1475,6 +1478,9 @@ extern "C" int reshape_and_cache(const void* k_new, const void* v_new, void* k_p
                                  void* stream) {
   if (num_tokens < 0 || num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
     return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache: negative size");
+  if (num_tokens > pa::kMaxWorkgroups)
+    return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache: %d tokens: one launch takes at most %d",
+                         num_tokens, pa::kMaxWorkgroups);
   if (num_kv_heads < 1 || !pa::head_dim_ok(head_dim))
     return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache: Hkv %d, head_dim %d", num_kv_heads, head_dim);
   if (!pa::block_size_ok(block_size))
@@ -1517,7 +1523,7 @@ extern "C" int paged_attn_decode(const void* q, const void* k_pages, const void*
                                   num_partials, workspace_bytes, workspace, max_blocks_per_seq))
     return rc;
   if (num_tasks == 0) return pa::clear_error();
-  if (!q || !k_pages || !v_pages || !block_table || !out || !tasks_dev ||
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out || !tasks_dev ||
       (num_combines > 0 && !combines_dev))
     return pa::set_error(PA_ERR_NULL, "paged_attn_decode: NULL pointer");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1589,6 +1595,10 @@ extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void*
                                      void* stream) {
   if (num_tokens < 0 || num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
     return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: negative size");
+  if (num_tokens > pa::kMaxWorkgroups)
+    return pa::set_error(PA_ERR_SHAPE,
+                         "reshape_and_cache_fp8: %d tokens: one launch takes at most %d",
+                         num_tokens, pa::kMaxWorkgroups);
   if (num_kv_heads < 1 || !pa::head_dim_ok(head_dim))
     return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: Hkv %d, head_dim %d", num_kv_heads,
                          head_dim);
@@ -1632,8 +1642,8 @@ extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const v
                                   num_partials, workspace_bytes, workspace, max_blocks_per_seq))
     return rc;
   if (num_tasks == 0) return pa::clear_error();
-  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !out ||
-      !tasks_dev || (num_combines > 0 && !combines_dev))
+  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !context_lens ||
+      !out || !tasks_dev || (num_combines > 0 && !combines_dev))
     return pa::set_error(PA_ERR_NULL, "paged_attn_decode_fp8: NULL pointer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, nullptr,

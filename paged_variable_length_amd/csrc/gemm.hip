@@ -412,6 +412,13 @@ extern "C" int smooth_gemm(const void* a, const void* w, void* c, int32_t M, int
     return pa::set_error(PA_ERR_SHAPE, "smooth_gemm: negative size or count");
   if (tile != 128 && tile != 256)
     return pa::set_error(PA_ERR_SHAPE, "smooth_gemm: tile %d must be 128 or 256", tile);
+  // the reduce launch runs tile^2 / (4 kReduceThreads) workgroups per record (each thread sums
+  // four columns of one row)
+  const int64_t reduce_groups =
+      static_cast<int64_t>(num_reduces) * tile * tile / (4 * kReduceThreads);
+  if (num_tasks > pa::kMaxWorkgroups || reduce_groups > pa::kMaxWorkgroups)
+    return pa::set_error(PA_ERR_SHAPE, "smooth_gemm: %d tasks, %d reduces exceed one launch",
+                         num_tasks, num_reduces);
   if (num_tasks == 0) return pa::clear_error();
   if (M == 0 || N == 0 || K == 0)
     return pa::set_error(PA_ERR_SHAPE, "smooth_gemm: tasks given for an empty product");

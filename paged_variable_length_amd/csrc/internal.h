@@ -25,5 +25,8 @@ constexpr int32_t kMaxGroup = 16;
 constexpr int32_t kMaxQTile = 128;
 // Key granularity of split boundaries (decode chunks and prefill key tiles both divide it).
 constexpr int32_t kSplitQuantum = 64;
+// Most workgroups one launch may have along its grid's x dimension: HIP keeps a dimension's
+// work-items (workgroups x threads) below 2^32, and the widest workgroup here has 512 threads.
+constexpr int32_t kMaxWorkgroups = (1 << 23) - 1;
 
 }  // namespace pa

@@ -201,8 +201,25 @@ def test_launcher_scalar_errors_need_no_gpu():
     assert L.paged_attn_decode(*args(2, 1, 64, 16, 0, 1, None, 0)) == _abi.PA_ERR_NULL
     assert L.paged_attn_decode(*args(2, 1, 64, 16, 0, 1, ctypes.c_void_p(16), 8)) == \
         _abi.PA_ERR_CAPACITY
-    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0)) == _abi.PA_ERR_NULL       # NULL q
-    assert b"NULL" in L.pa_last_error()
+    # a workspace is needed whenever the table has partial rows, combines or not
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0)) == _abi.PA_ERR_NULL
+    assert b"workspace" in L.pa_last_error()
+    ws = ctypes.c_void_p(256)
+    assert L.paged_attn_decode(*args(2, 1, 64, 16, 0, 0, ws, 1 << 20)) == _abi.PA_ERR_NULL  # q
+    assert b"NULL pointer" in L.pa_last_error()
+    # every device pointer but context_lens given: still refused before any launch
+    p = ctypes.c_void_p(256)
+    full = [p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, 0, p, 1, p, 1, 8, p, 1 << 20, p, None]
+    assert L.paged_attn_decode(*full) == _abi.PA_ERR_NULL
+    fp8 = full[:3] + [p, p] + full[3:12] + full[13:]
+    assert L.paged_attn_decode_fp8(*fp8) == _abi.PA_ERR_NULL
+    # one workgroup per task: 2^23 tasks exceed one launch
+    big = list(full)
+    big[5], big[14] = p, 1 << 23
+    assert L.paged_attn_decode(*big) == _abi.PA_ERR_SHAPE
+    assert b"at most 8388607" in L.pa_last_error()
+    rc = L.reshape_and_cache(p, p, p, p, p, 1, p, p, 1, 1 << 23, 1, 1, 64, 16, 0, None)
+    assert rc == _abi.PA_ERR_SHAPE
     v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, nul, 0, 0, nul, 0,
          nul, nul]
     assert L.paged_attn_varlen_prefill(*v) == _abi.PA_ERR_DTYPE                  # fp32 prefill

@@ -99,3 +99,10 @@ def test_gemm_launcher_scalar_errors_need_no_gpu():
     assert L.smooth_gemm(p, p, p, 4, 4, 4, 256, p, 2, p, 1, 2, p, 16, nul) == \
         _abi.PA_ERR_CAPACITY                                               # workspace too small
     assert b"workspace" in L.pa_last_error()
+    # launch limits: 2^23 tasks, or reduces whose 64 workgroups each (tile 256) pass 2^23 - 1
+    assert L.smooth_gemm(p, p, p, 4, 4, 4, 256, p, 1 << 23, nul, 0, 0, nul, 0, nul) == \
+        _abi.PA_ERR_SHAPE
+    assert L.smooth_gemm(p, p, p, 4, 4, 4, 256, p, 1, p, 1 << 17, 1, p, 1 << 40, nul) == \
+        _abi.PA_ERR_SHAPE
+    assert L.smooth_gemm(p, p, p, 4, 4, 4, 128, p, 1, p, 1 << 17, 1, p, 0, nul) == \
+        _abi.PA_ERR_CAPACITY                                               # 16 per record: fits
