@@ -67,8 +67,8 @@ TILING = {
 GEMM_TILING = {
     "gemm_linear_prefill_qproj": dict(tile=256, k_split=0),
     "gemm_linear_mixed_oproj": dict(tile=128, k_split=0),
-    "gemm_linear_1024x1024x1024": dict(tile=128, k_split=0),
-    "gemm_linear_512x2048x1024": dict(tile=128, k_split=0),
+    "gemm_linear_1024x1024x1024": dict(tile=128, k_split=256),
+    "gemm_linear_512x2048x1024": dict(tile=128, k_split=512),
     "gemm_linear_2048x512x2048": dict(tile=128, k_split=512),
 }
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")

@@ -45,6 +45,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kReduceThreads = 256;
+// Largest table run with the four-stage ring: one task per CU of the chip (256 CUs).
+constexpr int kDeepRingMaxTasks = 256;
 
 // Wave grid of a tile: WAVES_M x WAVES_N waves, each owning (TILE / WAVES_M) rows and
 // (TILE / WAVES_N) columns of the output tile.
@@ -115,12 +117,24 @@ __device__ __forceinline__ void lds_wait(u32x4 (&r)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
 }
 
+// Waits until at most N of this wave's vector memory operations are outstanding (N < 64).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima: no wait on them
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // TILE x TILE output tile per workgroup (128 or 256). ALIGNED: K % 8 == 0 and 16-byte aligned
 // bases, so every 16-byte chunk of a row is whole and aligned and stages load through direct
 // global->LDS loads; otherwise each lane gathers its chunk element by element into registers and
-// writes it (same layout, slower).
-template <int TILE, bool ALIGNED>
+// writes it (same layout, slower). NS: stage buffers per operand. With NS = 2 a stage's loads
+// are issued one stage ahead of its use; with NS = 4 (tile 128 only: 128 KiB of LDS, one
+// workgroup per CU, for tables with at most one task per CU) three stages ahead, so a stage of
+// small products no longer waits out the whole memory latency.
+template <int TILE, bool ALIGNED, int NS>
 __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(GemmArgs g) {
+  static_assert(NS == 2 || (NS == 4 && TILE == 128 && ALIGNED), "four stages: aligned tile 128");
   typedef GemmCfg<TILE> C;
   constexpr int WM = TILE / C::kWavesM;             // wave tile rows (m)
   constexpr int WN = TILE / C::kWavesN;             // wave tile columns (n)
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
   constexpr int kPieces = kTileBytes / 1024 / C::kWaves;   // 1 KiB loads per wave per operand
   static_assert(kPieces % 2 == 0, "pieces per wave must be even");
   constexpr int NOPS = NBN + NBM;                   // operand registers per k-step
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];   // A0 A1 W0 W1
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * kTileBytes];   // A0.. W0..
 
   const pa_gemm_task t = g.tasks[xcd_remap(blockIdx.x, g.num_tasks)];
   const int lane = threadIdx.x & 63;
@@ -162,7 +176,7 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
       const uint16_t* src = op == 0 ? g.a : g.w;
       const int base_row = op == 0 ? m0 : n0;
       const int nrows = op == 0 ? rows : cols;
-      char* tile = smem + (2 * op + buf) * kTileBytes;
+      char* tile = smem + (NS * op + buf) * kTileBytes;
       // every row of the tile exists and the stage is a whole 64: no lane is switched off
       const bool interior = nrows == TILE && ks + kBK <= k1;
       if constexpr (ALIGNED && C::kWaves == 8) {
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
   const int j = lane & 31, h = lane >> 5;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
   uint32_t a_base = lds0 + (WM * wm + j) * kRowBytes + (chunk_pos(j, h) << 4);
-  uint32_t w_base = lds0 + 2 * kTileBytes + (WN * wn + j) * kRowBytes + (chunk_pos(j, h) << 4);
+  uint32_t w_base = lds0 + NS * kTileBytes + (WN * wn + j) * kRowBytes + (chunk_pos(j, h) << 4);
 
   // operands of one k-step: [0, NBN) W blocks (n), [NBN, NBN + NBM) A blocks (m)
   typedef u32x4 Ops[NOPS];
@@ -263,19 +277,43 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
     }
   };
 
-  // ---- prologue: stages 0 and 1 in flight; wait for stage 0; operands of its first k-step
-  // (lanes switch loads off at the edges, so the number of loads a wave issues varies and
-  // every wait on them is a full wait)
-  load_stage(0, 0);
-  if (nst > 1) load_stage(1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
+  // Waits for this wave's loads of one stage while `after` later stages are in flight. A task
+  // whose every stage is interior issues kLoads loads per wave per stage, so the wait counts
+  // exactly; elsewhere lanes switch loads off at the edges and the wait is a full one.
+  constexpr int kLoads = 2 * kPieces;
+  const bool counted = NS > 2 && rows == TILE && cols == TILE && (k1 - k0) % kBK == 0;
+  auto wait_stage = [&](int after) {
+    if constexpr (NS > 2) {
+      if (counted) {
+        if (after == 3) {
+          vm_wait<3 * kLoads>();
+          return;
+        }
+        if (after == 2) {
+          vm_wait<2 * kLoads>();
+          return;
+        }
+        if (after == 1) {
+          vm_wait<kLoads>();
+          return;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  // ---- prologue: stages 0 .. NS-1 in flight; wait for stage 0; operands of its first k-step
+  for (int i = 0; i < NS; ++i)
+    if (i < nst) load_stage(i, i);
+  wait_stage(min(nst, NS) - 1);
   __builtin_amdgcn_s_barrier();
   Ops o0, o1;
   read_ops(0u, 0, o0);
 
-  // ---- stage s (operands of its k-step 0 already requested into o0), buffer s % 2
+  // ---- stage s (operands of its k-step 0 already requested into o0), buffer s % NS
   for (int s = 0; s < nst; ++s) {
-    const uint32_t cur = (s & 1) ? kTileBytes : 0u, nxt = kTileBytes - cur;
+    const uint32_t cur = static_cast<uint32_t>(s % NS) * kTileBytes;
+    const uint32_t nxt = static_cast<uint32_t>((s + 1) % NS) * kTileBytes;
     // opaque redefinition: the per-k-step addresses are recomputed where used instead of being
     // held in registers across the loop
     asm volatile("" : "+v"(a_base), "+v"(w_base));
@@ -294,12 +332,13 @@ __global__ __launch_bounds__(GemmCfg<TILE>::kThreads) void smooth_gemm_kernel(Ge
     // the loads of stage s+2 between the two halves of k-step 3.
     __builtin_amdgcn_sched_barrier(0);
     lds_wait<0>(o1);
-    __builtin_amdgcn_s_waitcnt(0);
+    // stages s+2 .. min(nst, s+NS) - 1 were issued after stage s+1
+    wait_stage(max(0, min(nst, s + NS) - s - 2));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     mfmas(o1, 0, NBN / 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (s + 2 < nst) load_stage(s + 2, s & 1);
+    if (s + NS < nst) load_stage(s + NS, s % NS);
     if (s + 1 < nst) read_ops(nxt, 0, o0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(o1, NBN / 2, NBN);
@@ -377,11 +416,16 @@ template <int TILE>
 int launch_gemm(const GemmArgs& g, bool aligned, const pa_gemm_reduce* reds, int32_t num_reduces,
                 hipStream_t st) {
   if (g.num_tasks > 0) {
-    if (aligned)
-      hipLaunchKernelGGL((smooth_gemm_kernel<TILE, true>), dim3(g.num_tasks),
+    // a tile-128 table of at most one task per CU runs with the deeper stage ring (one
+    // workgroup per CU)
+    if (TILE == 128 && aligned && g.num_tasks <= kDeepRingMaxTasks)
+      hipLaunchKernelGGL((smooth_gemm_kernel<128, true, 4>), dim3(g.num_tasks),
+                         dim3(GemmCfg<128>::kThreads), 0, st, g);
+    else if (aligned)
+      hipLaunchKernelGGL((smooth_gemm_kernel<TILE, true, 2>), dim3(g.num_tasks),
                          dim3(GemmCfg<TILE>::kThreads), 0, st, g);
     else
-      hipLaunchKernelGGL((smooth_gemm_kernel<TILE, false>), dim3(g.num_tasks),
+      hipLaunchKernelGGL((smooth_gemm_kernel<TILE, false, 2>), dim3(g.num_tasks),
                          dim3(GemmCfg<TILE>::kThreads), 0, st, g);
   }
   if (num_reduces > 0) {

@@ -78,7 +78,7 @@ def _run(M, N, K, tile, k_split, seed, a_offset=0, w_offset=0):
 @pytest.mark.parametrize("M,N,K,k_split", [
     (1, 1, 8, 0), (1, 300, 64, 0), (37, 19, 200, 0), (256, 256, 64, 0),
     (257, 513, 136, 0), (300, 200, 200, 128), (640, 384, 1000, 192), (513, 129, 4104, 1024),
-    (100, 700, 72, 64)])
+    (100, 700, 72, 64), (512, 384, 1024, 0), (384, 256, 1088, 320)])
 def test_gemm_ragged(M, N, K, k_split, tile):
     c, a, w, plan = _run(M, N, K, tile, k_split, seed=M + N + K)
     assert (len(plan.table.reduces) > 0) == (0 < k_split < K)
