@@ -61,16 +61,19 @@ TILING = {
     "decode_shared_mha_bf16:no_sharing": dict(dec_split=1024),
 }
 # SmoothGEMM (C = A W^T, bf16, fp32 accumulation) on Linear shapes: the pages' own Linear table
-# shapes and the q / o projections of this step's batches (synth.GEMM_SHAPES). Tile and K split
-# per shape from a sweep on MI355X: 256-wide tiles where there are enough of them to fill the
-# chip, 128-wide (and K pieces) where the product is small.
+# shapes and the q / o projections of this step's batches (synth.GEMM_SHAPES). Tiles per shape
+# from a sweep on MI355X: 256-wide where there are enough of them to fill the chip, 128-wide
+# where the product is small; in both, the blocks of the last partial round of 256 resident
+# workgroups are cut into K pieces (tail_split), which also gives the small products their K
+# pieces (256 or 512 deep).
 GEMM_TILING = {
-    "gemm_linear_prefill_qproj": dict(tile=256, k_split=0),
-    "gemm_linear_mixed_oproj": dict(tile=128, k_split=0),
-    "gemm_linear_1024x1024x1024": dict(tile=128, k_split=256),
-    "gemm_linear_512x2048x1024": dict(tile=128, k_split=512),
-    "gemm_linear_2048x512x2048": dict(tile=128, k_split=512),
+    "gemm_linear_prefill_qproj": dict(tile=256, k_split=0, tail_split=True),
+    "gemm_linear_mixed_oproj": dict(tile=256, k_split=0, tail_split=True),
+    "gemm_linear_1024x1024x1024": dict(tile=128, k_split=0, tail_split=True),
+    "gemm_linear_512x2048x1024": dict(tile=128, k_split=0, tail_split=True),
+    "gemm_linear_2048x512x2048": dict(tile=128, k_split=0, tail_split=True),
 }
+GEMM_WORKERS = 256      # resident workgroups: one per CU for both tiles
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
 
@@ -389,12 +392,14 @@ def run_gemm(name, steps, warmup, flush):
     tl = GEMM_TILING[name]
     a, w = synth.make_gemm_operands(M, N, K, device="cuda", seed=1)
     c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    plan = pa.GemmPlan(M, N, K, tile=tl["tile"], k_split=tl["k_split"], num_workers=256)
+    plan = pa.GemmPlan(M, N, K, tile=tl["tile"], k_split=tl["k_split"], num_workers=GEMM_WORKERS,
+                       tail_split=tl["tail_split"])
     nt = len(plan.table.tasks)
     pin = torch.zeros((max(nt, 1), 8), dtype=torch.int32, pin_memory=True)
 
     def step():
-        t = pa.build_gemm_table(M, N, K, tl["tile"], tl["k_split"], 256)
+        t = pa.build_gemm_table(M, N, K, tl["tile"], tl["k_split"], GEMM_WORKERS,
+                                tl["tail_split"])
         pin.numpy()[:nt] = t.tasks
         plan.tasks.copy_(pin[:nt], non_blocking=True)
         plan.run(a, w, c)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 enum pa_status {
   PA_OK = 0,
@@ -326,10 +326,15 @@ typedef struct pa_gemm_reduce {
  *   k_split     0: one task covers all of K; else a positive multiple of 64, the reduction
  *               length of one task (the page chains the K blocks of one output block by a
  *               dependency; here they are independent tasks whose partial tiles are summed)
- *   num_workers workers assumed by the balance report
- *   reserved    must be 0 */
+ *   num_workers workers (resident workgroups) assumed by the balance report and by tail_split
+ *   tail_split  0, or 1 with k_split 0: the blocks that fill the last, partial round of
+ *               num_workers (the last r = T mod W of the T whole blocks in load order; all of
+ *               them when T < W) are cut into p = min(W / r, ceil(K / 64)) K pieces when
+ *               p >= 2, each ceil(K / p) rounded up to a multiple of 64 (the last takes the
+ *               rest), so the last round holds up to W shorter tasks instead of r whole ones
+ *               (the page sizes blocks so that the sorted tasks keep every worker busy) */
 typedef struct pa_gemm_params {
-  int32_t tile, k_split, num_workers, reserved;
+  int32_t tile, k_split, num_workers, tail_split;
 } pa_gemm_params;
 
 /* The Linear decomposition (XY-Serve page, section 4.4, decompose_linear), on the host:
@@ -337,7 +342,7 @@ typedef struct pa_gemm_params {
  * stably sorted by load, descending. Partial slots are numbered in emission order, one per task
  * of an output block with more than one K piece, and each such block gets one reduce record
  * (emission order). Capacity and balance conventions as build_task_table.
- *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (tile, k_split, num_workers, reserved, negative sizes,
+ *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (tile, k_split, num_workers, tail_split, negative sizes,
  *   K = 0 with M, N > 0), PA_ERR_CAPACITY. M = 0 or N = 0 gives an empty table. Pure, no HIP
  *   calls. */
 int build_gemm_table(const pa_gemm_params* params, int32_t M, int32_t N, int32_t K,

@@ -376,10 +376,13 @@ class GemmTable:
     balance_modulo: float
 
 
-def build_gemm_table(M, N, K, tile=256, k_split=0, num_workers=256) -> GemmTable:
-    """Host Linear decomposition for C = A W^T (library call; sized by a first call)."""
+def build_gemm_table(M, N, K, tile=256, k_split=0, num_workers=256,
+                     tail_split=False) -> GemmTable:
+    """Host Linear decomposition for C = A W^T (library call; sized by a first call). With
+    ``tail_split`` the blocks of the last, partial round of ``num_workers`` are cut into K
+    pieces."""
     L = lib()
-    prm = PaGemmParams(int(tile), int(k_split), int(num_workers), 0)
+    prm = PaGemmParams(int(tile), int(k_split), int(num_workers), int(bool(tail_split)))
     nt, nr, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     rc = L.build_gemm_table(ctypes.byref(prm), int(M), int(N), int(K), None, 0, ctypes.byref(nt),
                             None, 0, ctypes.byref(nr), ctypes.byref(ns), None)
@@ -431,10 +434,11 @@ class GemmPlan:
     """A SmoothGEMM table for one (M, N, K) built on the host and copied to the device, with
     its workspace (torch allocations)."""
 
-    def __init__(self, M, N, K, tile=256, k_split=0, num_workers=256, device="cuda"):
+    def __init__(self, M, N, K, tile=256, k_split=0, num_workers=256, device="cuda",
+                 tail_split=False):
         torch = _torch()
         self.M, self.N, self.K, self.tile = int(M), int(N), int(K), int(tile)
-        self.table = build_gemm_table(M, N, K, tile, k_split, num_workers)
+        self.table = build_gemm_table(M, N, K, tile, k_split, num_workers, tail_split)
         self.tasks = torch.from_numpy(self.table.tasks).to(device)
         self.reduces = torch.from_numpy(self.table.reduces).to(device)
         nbytes = gemm_workspace_bytes(self.table.num_slots, tile)

@@ -25,7 +25,7 @@ PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -63,7 +63,7 @@ class PaGemmReduce(ctypes.Structure):
 
 
 class PaGemmParams(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("tile", "k_split", "num_workers", "reserved")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("tile", "k_split", "num_workers", "tail_split")]
 
 
 class PaParams(ctypes.Structure):

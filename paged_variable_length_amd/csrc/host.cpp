@@ -529,15 +529,46 @@ extern "C" int build_gemm_table(const pa_gemm_params* p, int32_t M, int32_t N, i
     return set_error(PA_ERR_SHAPE, "k_split %d must be 0 or a positive multiple of %d",
                      p->k_split, pa::kSplitQuantum);
   if (p->num_workers < 1) return set_error(PA_ERR_SHAPE, "num_workers must be >= 1");
-  if (p->reserved != 0) return set_error(PA_ERR_SHAPE, "pa_gemm_params.reserved must be zero");
+  if (p->tail_split != 0 && (p->tail_split != 1 || p->k_split != 0))
+    return set_error(PA_ERR_SHAPE, "tail_split must be 0, or 1 with k_split 0");
   if (M < 0 || N < 0 || K < 0) return set_error(PA_ERR_SHAPE, "negative size");
   if (K == 0 && M > 0 && N > 0)
     return set_error(PA_ERR_SHAPE, "K must be >= 1 for a non-empty product");
   const int64_t tile = p->tile;
-  const int64_t split = p->k_split > 0 ? p->k_split : std::max<int64_t>(K, 1);
   const int64_t mb = (M + tile - 1) / tile, nb = (N + tile - 1) / tile;
-  const int64_t nk = (K > 0 && M > 0 && N > 0) ? (K + split - 1) / split : 0;
-  const int64_t nt = mb * nb * nk, nr = nk > 1 ? mb * nb : 0, ns = nk > 1 ? nt : 0;
+  // output blocks in emission order (m block, n block); none when any size is zero
+  const int64_t T = (K > 0 && M > 0 && N > 0) ? mb * nb : 0;
+  if (T > INT32_MAX) return set_error(PA_ERR_SHAPE, "too many tasks");
+  auto rows_of = [&](int64_t b) { return std::min<int64_t>(tile, M - (b / nb) * tile); };
+  auto cols_of = [&](int64_t b) { return std::min<int64_t>(tile, N - (b % nb) * tile); };
+  // K piece length of each block: k_split, or all of K; with tail_split the blocks of the last,
+  // partial round of W workers (the last r = T mod W of the whole blocks in load order) are cut
+  // into p = min(W / r, ceil(K / 64)) pieces when p >= 2
+  const int64_t whole_split = p->k_split > 0 ? p->k_split : std::max<int64_t>(K, 1);
+  std::vector<int64_t> split(static_cast<size_t>(T), whole_split);
+  if (p->tail_split && T > 0) {
+    const int64_t W = p->num_workers, r = T % W;
+    const int64_t pieces = r ? std::min<int64_t>(W / r, (K + pa::kSplitQuantum - 1) / pa::kSplitQuantum) : 1;
+    if (pieces >= 2) {
+      const int64_t kp = ((K + pieces - 1) / pieces + pa::kSplitQuantum - 1) / pa::kSplitQuantum *
+                         pa::kSplitQuantum;
+      std::vector<uint32_t> whole(static_cast<size_t>(T));
+      std::iota(whole.begin(), whole.end(), 0u);
+      std::stable_sort(whole.begin(), whole.end(), [&](uint32_t x, uint32_t y) {
+        return rows_of(x) * cols_of(x) > rows_of(y) * cols_of(y);
+      });
+      for (int64_t i = T - r; i < T; ++i) split[whole[static_cast<size_t>(i)]] = kp;
+    }
+  }
+  int64_t nt = 0, nr = 0, ns = 0;
+  for (int64_t b = 0; b < T; ++b) {
+    const int64_t nk = (K + split[static_cast<size_t>(b)] - 1) / split[static_cast<size_t>(b)];
+    nt += nk;
+    if (nk > 1) {
+      ++nr;
+      ns += nk;
+    }
+  }
   if (nt > INT32_MAX) return set_error(PA_ERR_SHAPE, "too many tasks");
   *num_tasks = static_cast<int32_t>(nt);
   *num_reduces = static_cast<int32_t>(nr);
@@ -552,23 +583,23 @@ extern "C" int build_gemm_table(const pa_gemm_params* p, int32_t M, int32_t N, i
   emitted.reserve(static_cast<size_t>(nt));
   load.reserve(static_cast<size_t>(nt));
   int32_t slot = 0, r = 0;
-  for (int64_t m0 = 0; m0 < M && nk > 0; m0 += tile) {
-    const int32_t rows = static_cast<int32_t>(std::min<int64_t>(tile, M - m0));
-    for (int64_t n0 = 0; n0 < N; n0 += tile) {
-      const int32_t cols = static_cast<int32_t>(std::min<int64_t>(tile, N - n0));
-      const int32_t first = nk > 1 ? slot : -1;
-      if (nk > 1) {
-        reduces[r++] = pa_gemm_reduce{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
-                                      cols, first, static_cast<int32_t>(nk), 0, 0};
-        slot += static_cast<int32_t>(nk);
-      }
-      for (int64_t j = 0; j < nk; ++j) {
-        const int64_t k0 = j * split, k1 = std::min<int64_t>(K, k0 + split);
-        emitted.push_back(pa_gemm_task{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
-                                       cols, static_cast<int32_t>(k0), static_cast<int32_t>(k1),
-                                       nk > 1 ? first + static_cast<int32_t>(j) : -1, 0});
-        load.push_back(int64_t(rows) * cols * (k1 - k0));
-      }
+  for (int64_t b = 0; b < T; ++b) {
+    const int64_t m0 = (b / nb) * tile, n0 = (b % nb) * tile;
+    const int32_t rows = static_cast<int32_t>(rows_of(b)), cols = static_cast<int32_t>(cols_of(b));
+    const int64_t sp = split[static_cast<size_t>(b)];
+    const int64_t nk = (K + sp - 1) / sp;
+    const int32_t first = nk > 1 ? slot : -1;
+    if (nk > 1) {
+      reduces[r++] = pa_gemm_reduce{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
+                                    cols, first, static_cast<int32_t>(nk), 0, 0};
+      slot += static_cast<int32_t>(nk);
+    }
+    for (int64_t j = 0; j < nk; ++j) {
+      const int64_t k0 = j * sp, k1 = std::min<int64_t>(K, k0 + sp);
+      emitted.push_back(pa_gemm_task{static_cast<int32_t>(m0), rows, static_cast<int32_t>(n0),
+                                     cols, static_cast<int32_t>(k0), static_cast<int32_t>(k1),
+                                     nk > 1 ? first + static_cast<int32_t>(j) : -1, 0});
+      load.push_back(int64_t(rows) * cols * (k1 - k0));
     }
   }
   std::vector<uint32_t> order(emitted.size());

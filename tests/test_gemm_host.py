@@ -12,9 +12,10 @@ from paged_variable_length_amd import _abi
 from oracle import gemm as og
 
 
-def _both(M, N, K, tile, k_split, workers):
-    g = pa.build_gemm_table(M, N, K, tile, k_split, workers)
-    t, r, ns, _, bal = og.decompose_linear(og.GemmParams(tile, k_split, workers), M, N, K)
+def _both(M, N, K, tile, k_split, workers, tail=False):
+    g = pa.build_gemm_table(M, N, K, tile, k_split, workers, tail)
+    t, r, ns, _, bal = og.decompose_linear(og.GemmParams(tile, k_split, workers, int(tail)),
+                                           M, N, K)
     return g, (t, r, ns, bal)
 
 
@@ -40,6 +41,25 @@ def test_gemm_table_bit_exact_random(seed):
         assert np.array_equal(g.tasks, t) and np.array_equal(g.reduces, r) and g.num_slots == ns
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_gemm_table_tail_split_bit_exact_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(12):
+        M, N, K = (int(x) for x in rng.integers(1, 4000, size=3))
+        tile = int(rng.choice([128, 256]))
+        g, (t, r, ns, bal) = _both(M, N, K, tile, 0, int(rng.integers(1, 700)), tail=True)
+        assert np.array_equal(g.tasks, t) and np.array_equal(g.reduces, r) and g.num_slots == ns
+        assert g.balance_snake == pytest.approx(bal["snake"], abs=1e-12)
+
+
+def test_gemm_table_tail_split_on_the_bench_shapes():
+    for name in synth.GEMM_SHAPES:
+        M, N, K = synth.gemm_shape(name)
+        for tile in (128, 256):
+            g, (t, r, ns, _) = _both(M, N, K, tile, 0, 256, tail=True)
+            assert np.array_equal(g.tasks, t) and np.array_equal(g.reduces, r) and g.num_slots == ns
+
+
 def test_gemm_table_on_the_bench_shapes():
     for name in synth.GEMM_SHAPES:
         M, N, K = synth.gemm_shape(name)
@@ -60,9 +80,10 @@ def test_gemm_table_errors_match_oracle():
                                 None)
         assert rc == e.value.code == _abi.PA_ERR_SHAPE
     nt, nr, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    rc = L.build_gemm_table(ctypes.byref(_abi.PaGemmParams(256, 0, 1, 1)), 4, 4, 4, None, 0,
-                            ctypes.byref(nt), None, 0, ctypes.byref(nr), ctypes.byref(ns), None)
-    assert rc == _abi.PA_ERR_SHAPE      # reserved must be zero
+    for bad in (_abi.PaGemmParams(256, 0, 1, 2), _abi.PaGemmParams(256, 64, 1, 1)):
+        rc = L.build_gemm_table(ctypes.byref(bad), 4, 4, 4, None, 0, ctypes.byref(nt), None, 0,
+                                ctypes.byref(nr), ctypes.byref(ns), None)
+        assert rc == _abi.PA_ERR_SHAPE  # tail_split is 0, or 1 with k_split 0
     assert L.build_gemm_table(None, 4, 4, 4, None, 0, None, None, 0, None, None, None) == \
         _abi.PA_ERR_NULL
 

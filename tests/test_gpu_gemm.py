@@ -55,9 +55,9 @@ def _check(c, a, w, rows=None, what=""):
     return worst
 
 
-def _run(M, N, K, tile, k_split, seed, a_offset=0, w_offset=0):
+def _run(M, N, K, tile, k_split, seed, a_offset=0, w_offset=0, workers=256, tail=False):
     _announce(f"smooth_gemm M={M} N={N} K={K} tile={tile} k_split={k_split} "
-              f"offsets={a_offset},{w_offset}")
+              f"offsets={a_offset},{w_offset} workers={workers} tail={tail}")
     a0, w0 = synth.make_gemm_operands(M, N, K, device="cpu", seed=seed)
     # operands optionally start a few elements into a larger allocation (unaligned bases)
     abuf = torch.zeros(M * K + a_offset, dtype=torch.bfloat16, device=DEV)
@@ -66,7 +66,8 @@ def _run(M, N, K, tile, k_split, seed, a_offset=0, w_offset=0):
     w = wbuf[w_offset:].view(N, K)
     a.copy_(a0.to(DEV))
     w.copy_(w0.to(DEV))
-    plan = pa.GemmPlan(M, N, K, tile=tile, k_split=k_split, device=DEV)
+    plan = pa.GemmPlan(M, N, K, tile=tile, k_split=k_split, num_workers=workers, device=DEV,
+                       tail_split=tail)
     buf, c = _out_buffer(M, N)
     plan.run(a, w, c)
     torch.cuda.synchronize()
@@ -91,6 +92,15 @@ def test_gemm_unaligned_k(M, N, K, tile, k_split):
     """K not a multiple of 8: rows are not 16-byte aligned, so stages load element by element."""
     c, a, w, _ = _run(M, N, K, tile, k_split, seed=7 * K)
     _check(c, a, w, what=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,tile,workers", [(600, 512, 640, 256, 4), (1000, 64, 4097, 128, 40),
+                                                (1024, 1024, 1024, 128, 256),
+                                                (513, 700, 1000, 256, 3), (130, 260, 70, 128, 5)])
+def test_gemm_tail_split(M, N, K, tile, workers):
+    """Tables whose last partial round is cut into K pieces (reading of the page's balancing)."""
+    c, a, w, plan = _run(M, N, K, tile, 0, seed=M + K, workers=workers, tail=True)
+    _check(c, a, w, what=f"tail {M}x{N}x{K}")
 
 
 def test_gemm_unaligned_bases():
@@ -136,12 +146,14 @@ def test_gemm_closed_forms():
 
 @pytest.mark.parametrize("name", ["linear_mixed_oproj", "linear_prefill_qproj"])
 def test_gemm_full_size_sampled(name):
-    """The bench's Linear shapes at full size, in its launch configuration: sampled rows (first,
-    last and random rows) checked against the oracle, every element finite."""
+    """The bench's Linear shapes at full size, in its launch configuration (tile 256, the last
+    partial round cut into K pieces for 256 workers): sampled rows (first, last and random rows)
+    checked against the oracle, every element finite."""
     M, N, K = synth.gemm_shape(name)
     _announce(f"smooth_gemm full {name} {M}x{N}x{K}")
     a, w = synth.make_gemm_operands(M, N, K, device=DEV, seed=1)
-    plan = pa.GemmPlan(M, N, K, tile=256, k_split=0, device=DEV)
+    plan = pa.GemmPlan(M, N, K, tile=256, k_split=0, num_workers=256, device=DEV,
+                       tail_split=True)
     buf, c = _out_buffer(M, N)
     plan.run(a, w, c)
     torch.cuda.synchronize()

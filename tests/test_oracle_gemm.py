@@ -71,8 +71,57 @@ def test_coverage_and_loads(M, N, K, tile, k_split):
         assert mine == list(range(first, first + n))
 
 
+def test_hand_derived_tail_split():
+    """M=N=512, K=1000, tile 256, 3 workers, tail_split. Four equal blocks: one full round of 3
+    whole blocks, r = 4 mod 3 = 1 left over, p = min(3 // 1, ceil(1000/64) = 16) = 3 pieces of
+    ceil(1000/3) = 334 -> 384 keys: [0,384), [384,768), [768,1000). The tail block is the last
+    of the load-sorted whole blocks: all loads tie, so the last in emission order, (256, 256).
+    Loads: whole 256*256*1000 = 65536000; pieces 25165824, 25165824, 15204352."""
+    tasks, red, slots, loads, _ = og.decompose_linear(og.GemmParams(256, 0, 3, 1), 512, 512, 1000)
+    assert tasks.tolist() == [[0, 256, 0, 256, 0, 1000, -1, 0], [0, 256, 256, 256, 0, 1000, -1, 0],
+                              [256, 256, 0, 256, 0, 1000, -1, 0],
+                              [256, 256, 256, 256, 0, 384, 0, 0],
+                              [256, 256, 256, 256, 384, 768, 1, 0],
+                              [256, 256, 256, 256, 768, 1000, 2, 0]]
+    assert loads.tolist() == [65536000] * 3 + [25165824, 25165824, 15204352]
+    assert red.tolist() == [[256, 256, 256, 256, 0, 3, 0, 0]] and slots == 3
+
+
+def test_tail_split_cases():
+    # a whole number of rounds: nothing to cut
+    t, r, ns, _, _ = og.decompose_linear(og.GemmParams(128, 0, 4, 1), 256, 256, 512)
+    assert len(t) == 4 and ns == 0
+    # r > W / 2: p = 1, nothing to cut
+    t, r, ns, _, _ = og.decompose_linear(og.GemmParams(128, 0, 5, 1), 384, 384, 512)
+    assert len(t) == 9 and ns == 0
+    # fewer blocks than workers: all are cut; pieces capped by ceil(K / 64)
+    t, r, ns, _, _ = og.decompose_linear(og.GemmParams(128, 0, 64, 1), 128, 256, 100)
+    assert sorted((x[4], x[5]) for x in t.tolist()) == [(0, 64), (0, 64), (64, 100), (64, 100)]
+    # edge blocks are lighter, sort last and are the ones cut: 3 x 2 blocks, 4 workers
+    t, r, ns, _, _ = og.decompose_linear(og.GemmParams(256, 0, 4, 1), 600, 512, 640)
+    cut = {(x[0], x[2]) for x in t.tolist() if x[6] >= 0}
+    assert cut == {(512, 0), (512, 256)}
+
+
+@pytest.mark.parametrize("M,N,K,tile,W", [(1, 1, 1, 128, 7), (257, 129, 300, 128, 5),
+                                          (513, 700, 1000, 256, 3), (1000, 64, 4097, 128, 40)])
+def test_tail_split_coverage(M, N, K, tile, W):
+    """Every (m, n, k) is covered once, pieces are multiples of 64 but the last, and the tasks
+    after the last whole round number at most W."""
+    tasks, red, slots, loads, _ = og.decompose_linear(og.GemmParams(tile, 0, W, 1), M, N, K)
+    cover = np.zeros((M, N, K), dtype=np.int32)
+    for m0, rows, n0, cols, k0, k1, slot, _ in tasks.tolist():
+        cover[m0:m0 + rows, n0:n0 + cols, k0:k1] += 1
+        assert k0 % 64 == 0 and (k1 == K or (k1 - k0) % 64 == 0)
+    assert np.all(cover == 1) and int(loads.sum()) == M * N * K
+    T = -(-M // tile) * -(-N // tile)
+    assert len(tasks) - (T // W) * W <= W
+    assert slots == sum(x[5] for x in red.tolist())
+
+
 def test_errors():
-    for p in (og.GemmParams(64, 0), og.GemmParams(256, 32), og.GemmParams(256, 0, 0)):
+    for p in (og.GemmParams(64, 0), og.GemmParams(256, 32), og.GemmParams(256, 0, 0),
+              og.GemmParams(256, 64, 4, 1), og.GemmParams(256, 0, 4, 2)):
         with pytest.raises(og.GemmTableError) as e:
             og.decompose_linear(p, 4, 4, 4)
         assert e.value.code == og.ERR_SHAPE
