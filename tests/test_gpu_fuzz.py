@@ -1,0 +1,56 @@
+"""GPU parity on seeded random batches: the parameter space the fixed cases sample by hand
+(head dim, block size, GQA group, split sizes, query tile, verify rows, the mix of decode,
+draft and prefill rows), drawn jointly, each batch checked against the fp64 oracle at the same
+bars as the fixed cases. Every case prints its seed and shapes before it runs."""
+import numpy as np
+import pytest
+
+import synth
+from tests.test_gpu_parity import small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(rng, max_seqs, decode_only):
+    n = int(rng.integers(1, max_seqs + 1))
+    q, ctx = [], []
+    for _ in range(n):
+        kind = 0 if decode_only else int(rng.choice(3, p=[0.5, 0.2, 0.3]))
+        ql = 1 if kind == 0 else (int(rng.integers(2, 5)) if kind == 1 else int(rng.integers(5, 300)))
+        prefix = int(rng.integers(0 if ql > 1 else 1, 1500))
+        q.append(ql)
+        ctx.append(ql + prefix - (1 if ql == 1 else 0))
+    return q, ctx
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_mixed_batches(seed):
+    """Unified launch (bf16) over a random mix of decode rows, short drafts and prefill chunks."""
+    rng = np.random.default_rng(7000 + seed)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    q, ctx = _batch(rng, 10, decode_only=False)
+    tiling = dict(dec_split=int(rng.choice([64, 128, 512, 4096])),
+                  pf_q_tile=int(rng.choice([16, 64, 100, 128])),
+                  pf_kv_split=int(rng.choice([0, 64, 192, 512])),
+                  verify_rows=int(rng.choice([0, 4, 8])))
+    w = synth.custom_workload(q, ctx, hkv * g, hkv, d, bs, seed=seed,
+                              spare_blocks=int(rng.integers(0, 4)))
+    small_case(w, "varlen", **tiling)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_random_decode_batches(seed, dtype):
+    """Decode entry over random single-row batches (bf16 and fp32 pages)."""
+    rng = np.random.default_rng(8000 + seed)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8, 16]))
+    q, ctx = _batch(rng, 16, decode_only=True)
+    w = synth.custom_workload(q, ctx, hkv * g, hkv, d, bs, dtype=dtype, seed=seed,
+                              spare_blocks=int(rng.integers(0, 4)))
+    small_case(w, "decode", dec_split=int(rng.choice([64, 256, 1024])))
