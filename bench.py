@@ -37,6 +37,7 @@ METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
              "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8",
+             "verify_gqa_fp8",
              "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing",
              "gemm_linear_prefill_qproj", "gemm_linear_mixed_oproj", "gemm_linear_1024x1024x1024",
              "gemm_linear_512x2048x1024", "gemm_linear_2048x512x2048"]
@@ -53,8 +54,10 @@ TILING = {
     # for comparison the same batch decomposed into prefill tiles (one per query head)
     "verify_gqa_bf16": dict(dec_split=8192, verify_rows=4),
     "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
-    # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline)
+    # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline), and the
+    # verify batch over fp8 pages
     "decode_mha_fp8": dict(dec_split=1024),
+    "verify_gqa_fp8": dict(dec_split=8192, verify_rows=4),
     # 8 prompts x 16 decoding requests that alias the prompt's blocks: the prefix is read once
     # per group and kv head; the variant runs the same batch without grouping
     "decode_shared_mha_bf16": dict(dec_split=4096, shared_min=64),
@@ -236,10 +239,14 @@ class Runner:
         combines = self.dev[k][self.cap_t:self.cap_t + nc]
         if ev_pair is not None:
             ev_pair[0].record()
-        if self.fp8:
+        if self.fp8 and self.decode_only:
             pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
                                      v["v_scales"], self.bt, self.ctx, self.scale, tasks,
                                      combines, nparts, self.ws, self.out)
+        elif self.fp8:
+            pa.paged_attn_verify_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
+                                     v["v_scales"], self.bt, self.cu, self.ctx, self.scale,
+                                     tasks, combines, nparts, self.ws, self.out)
         elif self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
                                  tasks, combines, nparts, self.ws, self.out)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 
 enum pa_status {
   PA_OK = 0,
@@ -284,6 +284,27 @@ int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_page
                           const float* k_scales, const float* v_scales,
                           const int32_t* block_table, int32_t max_blocks_per_seq,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          float scale, const pa_task* tasks_dev, int32_t num_tasks,
+                          const pa_combine* combines_dev, int32_t num_combines,
+                          int32_t num_partials, void* workspace, size_t workspace_bytes,
+                          void* out, void* stream);
+
+/* Speculative-verify rows over fp8 pages (ATB page, speculative decoding: the target model scores
+ * a draft's tokens in one step; cann-recipes-infer page, section 5.2: values read as code times
+ * their page's scale): as paged_attn_varlen_prefill for a batch of decode rows and short drafts,
+ * q and out bf16 [num_tokens, Hq, D] packed by cu_seqlens_q, with the pages, scales and value
+ * reading of paged_attn_decode_fp8. Runs the PA_TASK_DECODE and PA_TASK_VERIFY tasks of the table
+ * (built with verify_rows > 0): each verify row sees the keys up to and including its own
+ * position. Prefill and shared-prefix tasks are not run and their outputs are not written.
+ *   Device pointers: q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
+ *   context_lens, tasks_dev, combines_dev, workspace, out.
+ *   Errors as paged_attn_decode_fp8, plus PA_ERR_SHAPE for num_tokens < num_seqs. */
+int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_pages,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           float scale, const pa_task* tasks_dev, int32_t num_tasks,
                           const pa_combine* combines_dev, int32_t num_combines,

@@ -32,7 +32,7 @@ from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
            "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
-           "reshape_and_cache_fp8", "paged_attn_decode_fp8",
+           "reshape_and_cache_fp8", "paged_attn_decode_fp8", "paged_attn_verify_fp8",
            "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32",
            "build_gemm_table", "gemm_workspace_bytes", "smooth_gemm", "GemmTable", "GemmPlan"]
 
@@ -285,6 +285,35 @@ def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, 
     check(lib().paged_attn_decode_fp8(*args), "paged_attn_decode_fp8")
 
 
+def paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
+                          context_lens, scale, tasks_dev, combines_dev, num_partials, workspace,
+                          out, stream=None):
+    """Decode rows and speculative drafts over fp8 pages with page scales (library kernels).
+    q/out bf16 [T, Hq, D] packed by cu_seqlens_q; pages uint8 [NB, Hkv, bs, D]; scales
+    float32 [NB, Hkv]. Runs the table's decode and verify tasks only."""
+    torch = _torch()
+    if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
+        raise ValueError("k_pages and v_pages must both be [NB, Hkv, bs, D]")
+    if q.dim() != 3 or out.shape != q.shape or q.shape[2] != k_pages.shape[3]:
+        raise ValueError("q and out must both be [T, Hq, D] with the pages' head_dim")
+    nb, hkv = k_pages.shape[:2]
+    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
+        raise ValueError("page scales must be [num_blocks, Hkv]")
+    t, hq, d = q.shape
+    n = context_lens.shape[0]
+    if cu_seqlens_q.shape[0] != n + 1 or block_table.dim() != 2 or block_table.shape[0] != n:
+        raise ValueError("block_table / cu_seqlens_q / context_lens sizes disagree")
+    args = [_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
+            _dev(v_pages, "v_pages", torch.uint8), _dev(k_scales, "k_scales", torch.float32),
+            _dev(v_scales, "v_scales", torch.float32),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32), n, t, hq, hkv, d, k_pages.shape[2],
+            float(scale)] + _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        [_dev(out, "out", torch.bfloat16), _stream(stream)]
+    check(lib().paged_attn_verify_fp8(*args), "paged_attn_verify_fp8")
+
+
 def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
                               scale, tasks_dev, combines_dev, num_partials, workspace, out,
                               stream=None):
@@ -357,6 +386,15 @@ class StepPlan:
     def decode_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
         self._check_decode_table("decode_fp8")
         paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table,
+                              self.ctx, scale, self.tasks, self.combines, self.num_partials,
+                              self.workspace, out, stream)
+
+    def verify_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
+        kinds = set(np.unique(self.table.tasks[:, 0]).tolist()) if len(self.table.tasks) else set()
+        if not kinds <= {PA_TASK_DECODE, PA_TASK_VERIFY}:
+            raise ValueError("verify_fp8 runs decode and verify tasks only: build the table with "
+                             "verify_rows covering every draft and shared_min 0")
+        paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table, self.cu,
                               self.ctx, scale, self.tasks, self.combines, self.num_partials,
                               self.workspace, out, stream)
 

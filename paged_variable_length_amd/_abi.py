@@ -25,7 +25,7 @@ PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -37,7 +37,7 @@ ERROR_NAMES = {
 EXPORTS = ("pa_abi_version", "pa_last_error", "pa_pack_seqlens", "build_task_table",
            "pa_workspace_bytes", "reshape_and_cache", "paged_attn_decode",
            "paged_attn_varlen_prefill", "pa_validate_block_table", "reshape_and_cache_fp8",
-           "paged_attn_decode_fp8",
+           "paged_attn_decode_fp8", "paged_attn_verify_fp8",
            "build_task_table_shared", "build_gemm_table", "pa_gemm_workspace_bytes",
            "smooth_gemm")
 
@@ -129,6 +129,10 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
                                         ctypes.c_float, p, i32, p, i32, i32, p, ctypes.c_size_t,
                                         p, p]
+    L.paged_attn_verify_fp8.restype = ctypes.c_int
+    L.paged_attn_verify_fp8.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                                        i32, ctypes.c_float, p, i32, p, i32, i32, p,
+                                        ctypes.c_size_t, p, p]
     L.pa_validate_block_table.restype = ctypes.c_int
     L.pa_validate_block_table.argtypes = [pi32, i32, pi32, i32, i32, i32]
     L.build_gemm_table.restype = ctypes.c_int

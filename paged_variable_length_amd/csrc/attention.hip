@@ -328,7 +328,8 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
 //   every code becomes bf16 with its page scale applied in the same exact conversion;
 //   a wave loads the raw codes of its next chunk before it computes the current one, and the
 //   block ids of the chunk after that, so a chunk of loads is always in flight per wave.
-// Decode tasks only (one query row per sequence).
+// Decode and verify tasks: as in the bf16 body, the 16 columns are (query row, head) pairs of the
+// task's q_rows rows (one for decode), each masking the keys after its row's position.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct Fp8VRaw;
@@ -370,18 +371,25 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
   const int s = t.seq, kvh = t.head;
   const int tok = a.cu_seqlens ? a.cu_seqlens[s] : s;
   const int bs = a.block_size;
+  const int nrows = t.q_rows;
+  const int ncol = nrows * G;
+  const int row = i16 / G, hh = i16 - row * G;     // this lane's score column
 
   bf16x8 qf[KS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(tok) * a.num_q_heads + kvh * G + i16) * D + 16 * g4;
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) +
+        (static_cast<size_t>(tok + row) * a.num_q_heads + kvh * G + hh) * D + 16 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (i16 < G) v = *reinterpret_cast<const u32x4*>(qp + 64 * (ks >> 1) + 8 * (ks & 1));
+      if (i16 < ncol) v = *reinterpret_cast<const u32x4*>(qp + 64 * (ks >> 1) + 8 * (ks & 1));
       qf[ks] = as_bf16x8(v);
     }
   }
+  // causal limit of this column (its row sits at position ctx - nrows + row; decode: every key)
+  const int key_lim = a.context_lens[s] - nrows + row + 1;
+  const int lim_lo = a.context_lens[s] - nrows + 1;
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pages) + kvh * head_stride;
@@ -453,17 +461,28 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
         }
       }
     }
+    if (cs + 32 > lim_lo) {
+      // keys after a verify row's own position get no weight in that row's column (their
+      // values are finite: they lie below kv1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = cs + 16 * (e >> 2) + 4 * g4 + (e & 3);
+        if (key >= key_lim) sc[e >> 2][e & 3] = -INFINITY;
+      }
+    }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx * c);
-    const float alpha = fast_exp2(m - mnew);
+    // a verify column can have seen no key yet (every score -inf): weights 0, not NaN
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(m - muse);
     float p[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], c, -mnew));
+      p[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], c, -muse));
       psum += p[e];
     }
     l = l * alpha + psum;
@@ -526,7 +545,7 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
       bn[1] = bn2[1];
     }
   }
-  decode_merge_and_store<D>(a, t, tok, G, G, m, l, acc, smem, true);
+  decode_merge_and_store<D>(a, t, tok, G, ncol, m, l, acc, smem, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1205,7 +1224,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
   __shared__ float smem[128 + 4 * 16 * D];
   const pa_task t = a.tasks[blockIdx.x];
-  if (t.kind != PA_TASK_DECODE) return;
+  // verify tasks need the packed rows' offsets (cu_seqlens), which only the verify entry passes
+  if (t.kind != PA_TASK_DECODE && !(t.kind == PA_TASK_VERIFY && a.cu_seqlens)) return;
   decode_task_fp8<D>(a, t, smem);
 }
 
@@ -1659,4 +1679,41 @@ extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const v
     launch_combine<__bf16, 64>(combines_dev, num_combines, nullptr, a, st);
   }
   return hip_check("paged_attn_decode_fp8");
+}
+
+extern "C" int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     float scale, const pa_task* tasks_dev, int32_t num_tasks,
+                                     const pa_combine* combines_dev, int32_t num_combines,
+                                     int32_t num_partials, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream) {
+  if (int rc = check_attn_scalars("paged_attn_verify_fp8", num_seqs, num_q_heads, num_kv_heads,
+                                  head_dim, block_size, PA_BF16, num_tasks, num_combines,
+                                  num_partials, workspace_bytes, workspace, max_blocks_per_seq))
+    return rc;
+  if (num_tokens < num_seqs)
+    return pa::set_error(PA_ERR_SHAPE, "paged_attn_verify_fp8: %d tokens for %d sequences",
+                         num_tokens, num_seqs);
+  if (num_tasks == 0) return pa::clear_error();
+  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !cu_seqlens_q ||
+      !context_lens || !out || !tasks_dev || (num_combines > 0 && !combines_dev))
+    return pa::set_error(PA_ERR_NULL, "paged_attn_verify_fp8: NULL pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
+                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                         tasks_dev, num_tasks, num_partials, workspace, out);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(decode_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
+  } else {
+    hipLaunchKernelGGL(decode_fp8_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
+  }
+  return hip_check("paged_attn_verify_fp8");
 }

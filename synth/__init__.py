@@ -108,9 +108,10 @@ def _lengths(name: str, rng: np.random.Generator):
         # the MHA decode batch (same lengths) over fp8 pages with per-page scales
         ctx = rng.integers(128, 4097, size=64).astype(np.int64)
         return np.ones(64, np.int64), ctx, 32, 32, 128, 16, "bf16", None
-    if name == "verify_gqa_bf16":
+    if name in ("verify_gqa_bf16", "verify_gqa_fp8"):
         # the GQA decode batch with a 4-row draft per sequence (3 drafted tokens plus the last
-        # accepted one) verified in one step; contexts include the draft rows
+        # accepted one) verified in one step; contexts include the draft rows (the fp8 variant
+        # has the same lengths, over fp8 pages with per-page scales)
         u = rng.uniform(math.log(64.0), math.log(32768.0), size=256)
         ctx = np.clip(np.floor(np.exp(u)), 64, 32768).astype(np.int64)
         return np.full(256, 4, np.int64), ctx, 32, 8, 128, 16, "bf16", None
@@ -126,6 +127,7 @@ WORKLOADS = {
     "prefill_varlen_bf16": 4,
     "mixed_bf16": 5,
     "verify_gqa_bf16": 6,
+    "verify_gqa_fp8": 6,
     "decode_mha_fp8": 2,
     "decode_shared_mha_bf16": 7,
 }

@@ -135,3 +135,58 @@ def test_decode_fp8_full_size_sampled():
                       rng.choice(w.num_seqs, 10, replace=False).tolist()))
     _, out = _decode_case(w, 1024, seqs)
     assert torch.isfinite(out).all()
+
+
+def _verify_case(w, dec_split, verify_rows, seqs=None):
+    """Cache write, then decode rows and drafts over fp8 pages through paged_attn_verify_fp8,
+    against the fp64 oracle on the oracle's dequantized pages (all rows of `seqs`)."""
+    vals = {k: v.to(DEV) for k, v in synth.make_values(w, device="cpu").items()}
+    pages = {k: v.to(DEV) for k, v in synth.make_fp8_pages(w).items()}
+    kc, vc, ks, vs = _oracle_write(w, vals, pages)
+    plan = pa.StepPlan(w.q_lens, w.ctx_lens, w.block_table, w.num_q_heads, w.num_kv_heads,
+                       w.head_dim, w.block_size, device=DEV, dec_split=dec_split,
+                       verify_rows=verify_rows)
+    _gpu_write(w, vals, pages, plan)
+    out = torch.full_like(vals["q"], float("nan"))
+    scale = 1.0 / math.sqrt(w.head_dim)
+    plan.verify_fp8(vals["q"], pages["k_codes"], pages["v_codes"], pages["k_scales"],
+                    pages["v_scales"], scale, out)
+    torch.cuda.synchronize()
+    seqs = list(range(w.num_seqs)) if seqs is None else seqs
+    cu = oa.pack_lengths(w.q_lens)
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    kp, table = _subset(kc, ks, w, seqs)
+    vp, _ = _subset(vc, vs, w, seqs)
+    ref = oa.paged_attention_fast(to_np(vals["q"])[rows], kp, vp, table, w.q_lens[seqs],
+                                  w.ctx_lens[seqs], scale)
+    return check_close(to_np(out)[rows], ref, "bf16", w.name), out
+
+
+@pytest.mark.parametrize("d,hq,hkv,bs", [(128, 32, 8, 16), (128, 8, 8, 64), (64, 16, 2, 16),
+                                         (128, 16, 1, 128)])
+@pytest.mark.parametrize("dec_split", [64, 512])
+def test_verify_fp8_ragged(d, hq, hkv, bs, dec_split):
+    """Drafts of 2 .. min(8, 16 / G) rows and single decode rows over ragged contexts."""
+    g = hq // hkv
+    longest = min(8, 16 // g)
+    rng = np.random.default_rng(d + hq + bs + dec_split)
+    ctx = [50, 300, 17, 1000, 4, 65, 129, 700, 2]
+    q = [1 if i % 3 == 2 or longest < 2 else int(rng.integers(2, longest + 1))
+         for i in range(len(ctx))]
+    ctx = [max(c, ql) for c, ql in zip(ctx, q)]
+    w = synth.custom_workload(q, ctx, hq, hkv, d, bs, seed=d + hq + bs, spare_blocks=3)
+    _announce(f"fp8 verify D={d} Hq={hq} Hkv={hkv} bs={bs} dec_split={dec_split} q={q}")
+    _verify_case(w, dec_split, max(2, longest))
+
+
+def test_verify_fp8_full_size_sampled():
+    """The 256-sequence GQA verify batch (4 draft rows each) over fp8 pages in the benchmark's
+    configuration; a seeded sample of sequences (shortest and longest included)."""
+    w = synth.make_workload("verify_gqa_fp8")
+    _announce(f"fp8 verify full N={w.num_seqs} T={w.num_tokens} NB={w.num_blocks}")
+    rng = np.random.default_rng(6)
+    order = np.argsort(w.ctx_lens)
+    seqs = sorted(set([int(order[0]), int(order[-1])] +
+                      rng.choice(w.num_seqs, 10, replace=False).tolist()))
+    _, out = _verify_case(w, 8192, 4, seqs)
+    assert torch.isfinite(out).all()
