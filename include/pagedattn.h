@@ -90,8 +90,8 @@ enum pa_task_kind {
  *           automatic prefix cache; ATB page, KV cache reuse), for their single query rows and
  *           all Hq/Hkv query heads of kv head `head`: the pages are read once for all of them.
  *           Always writes partials: member i, head j goes to row partial + i*q_row0 + j (q_row0
- *           holds the member stride). paged_attn_decode and paged_attn_varlen_prefill run
- *           these tasks; paged_attn_decode_fp8 does not.
+ *           holds the member stride). paged_attn_decode, paged_attn_varlen_prefill and
+ *           paged_attn_decode_fp8 run these tasks.
  *   partial -1: the task sees all keys its rows need and writes `out` directly.
  *           >= 0: first workspace row of this task's partial result (one row per
  *           (query row, head) pair it covers); split_combine merges the partials. */
@@ -278,8 +278,8 @@ int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages, v
 
 /* Decode attention over fp8 pages: as paged_attn_decode with dtype PA_BF16 for q and out, each
  * cached value read as code * page scale (an exact bf16 value, converted on load). The task
- * table is one built with verify_rows = 0: the kernel runs PA_TASK_DECODE rows only, and the
- * outputs of any other kind are not written. Errors as paged_attn_decode. */
+ * table is one built with verify_rows = 0: the kernel runs PA_TASK_DECODE and PA_TASK_SHARED
+ * tasks, and the outputs of any other kind are not written. Errors as paged_attn_decode. */
 int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
                           const float* k_scales, const float* v_scales,
                           const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -371,8 +371,6 @@ class StepPlan:
         if not self.decode_only or self.params.verify_rows:
             raise ValueError(f"{who} runs decode tasks only: every q_len must be 1 and "
                              "verify_rows 0 (use varlen for other batches)")
-        if who == "decode_fp8" and self.params.shared_min:
-            raise ValueError("decode_fp8 runs no shared-prefix tasks: build with shared_min 0")
 
     def decode(self, q, k_pages, v_pages, scale, out, stream=None):
         self._check_decode_table("decode")

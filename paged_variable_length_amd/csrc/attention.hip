@@ -328,8 +328,10 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
 //   every code becomes bf16 with its page scale applied in the same exact conversion;
 //   a wave loads the raw codes of its next chunk before it computes the current one, and the
 //   block ids of the chunk after that, so a chunk of loads is always in flight per wave.
-// Decode and verify tasks: as in the bf16 body, the 16 columns are (query row, head) pairs of the
-// task's q_rows rows (one for decode), each masking the keys after its row's position.
+// Decode, verify and shared-prefix tasks: as in the bf16 body, the 16 columns are (query row,
+// head) pairs of the task's q_rows rows (one for decode; the members' single rows for a shared
+// prefix), each masking the keys after its row's position (a shared prefix lies below every
+// member's row: no limit).
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct Fp8VRaw;
@@ -388,8 +390,9 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
     }
   }
   // causal limit of this column (its row sits at position ctx - nrows + row; decode: every key)
-  const int key_lim = a.context_lens[s] - nrows + row + 1;
-  const int lim_lo = a.context_lens[s] - nrows + 1;
+  const bool shared = t.kind == PA_TASK_SHARED;
+  const int key_lim = shared ? INT_MAX : a.context_lens[s] - nrows + row + 1;
+  const int lim_lo = shared ? INT_MAX : a.context_lens[s] - nrows + 1;
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pages) + kvh * head_stride;
@@ -1224,8 +1227,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
   __shared__ float smem[128 + 4 * 16 * D];
   const pa_task t = a.tasks[blockIdx.x];
-  // verify tasks need the packed rows' offsets (cu_seqlens), which only the verify entry passes
-  if (t.kind != PA_TASK_DECODE && !(t.kind == PA_TASK_VERIFY && a.cu_seqlens)) return;
+  // verify tasks need the packed rows' offsets (cu_seqlens), which only the verify entry passes;
+  // shared-prefix tasks address their members' rows as consecutive decode rows (no cu_seqlens)
+  if (t.kind == PA_TASK_PREFILL || (t.kind == PA_TASK_VERIFY && !a.cu_seqlens) ||
+      (t.kind == PA_TASK_SHARED && a.cu_seqlens))
+    return;
   decode_task_fp8<D>(a, t, smem);
 }
 

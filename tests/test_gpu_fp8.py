@@ -9,6 +9,7 @@ import torch
 
 import synth
 import paged_variable_length_amd as pa
+from paged_variable_length_amd import _abi
 from oracle import attention as oa
 from oracle import fp8 as of
 from tests.helpers import check_close, to_np
@@ -93,12 +94,12 @@ def _subset(codes, scales, w, seqs):
     return of.dequantize_pages(codes[idx], scales[idx]), table
 
 
-def _decode_case(w, dec_split, seqs=None):
+def _decode_case(w, dec_split, seqs=None, **tiling):
     vals = {k: v.to(DEV) for k, v in synth.make_values(w, device="cpu").items()}
     pages = {k: v.to(DEV) for k, v in synth.make_fp8_pages(w).items()}
     kc, vc, ks, vs = _oracle_write(w, vals, pages)
     plan = pa.StepPlan(w.q_lens, w.ctx_lens, w.block_table, w.num_q_heads, w.num_kv_heads,
-                       w.head_dim, w.block_size, device=DEV, dec_split=dec_split)
+                       w.head_dim, w.block_size, device=DEV, dec_split=dec_split, **tiling)
     _gpu_write(w, vals, pages, plan)
     out = torch.full_like(vals["q"], float("nan"))
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -110,7 +111,7 @@ def _decode_case(w, dec_split, seqs=None):
     vp, _ = _subset(vc, vs, w, seqs)
     q = to_np(vals["q"])[seqs]
     ref = oa.paged_attention_fast(q, kp, vp, table, w.q_lens[seqs], w.ctx_lens[seqs], scale)
-    return check_close(to_np(out)[seqs], ref, "bf16", w.name), out
+    return check_close(to_np(out)[seqs], ref, "bf16", w.name), out, plan
 
 
 @pytest.mark.parametrize("d,hq,hkv,bs", [(128, 8, 2, 16), (128, 32, 32, 16), (64, 16, 4, 64),
@@ -133,7 +134,7 @@ def test_decode_fp8_full_size_sampled():
     order = np.argsort(w.ctx_lens)
     seqs = sorted(set([int(order[0]), int(order[-1])] +
                       rng.choice(w.num_seqs, 10, replace=False).tolist()))
-    _, out = _decode_case(w, 1024, seqs)
+    _, out, _ = _decode_case(w, 1024, seqs)
     assert torch.isfinite(out).all()
 
 
@@ -190,3 +191,18 @@ def test_verify_fp8_full_size_sampled():
                       rng.choice(w.num_seqs, 10, replace=False).tolist()))
     _, out = _verify_case(w, 8192, 4, seqs)
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,dec_split", [(8, 8, 128, 16, 64), (16, 4, 64, 32, 64),
+                                                   (32, 4, 128, 16, 128)])
+def test_shared_decode_fp8(hq, hkv, d, bs, dec_split):
+    """Decode sequences whose tables alias a prompt's blocks, over fp8 pages: the prefix runs as
+    shared-prefix tasks read once per group and kv head (their rows are the members' own)."""
+    rng = np.random.default_rng(hq * 10 + bs + d)
+    prefix = rng.integers(1, 40, size=5) * bs
+    own = [rng.integers(1, 300, size=int(rng.integers(1, 21))) for _ in range(5)]
+    w = synth.shared_prefix_workload(prefix, own, hq, hkv, d, bs, seed=int(rng.integers(1 << 30)),
+                                     spare_blocks=3)
+    _announce(f"fp8 shared decode Hq={hq} Hkv={hkv} D={d} bs={bs} groups={prefix.tolist()}")
+    _, out, plan = _decode_case(w, dec_split, shared_min=64)
+    assert np.any(plan.table.tasks[:, 0] == _abi.PA_TASK_SHARED)
