@@ -220,6 +220,15 @@ def test_launcher_scalar_errors_need_no_gpu():
     assert b"at most 8388607" in L.pa_last_error()
     rc = L.reshape_and_cache(p, p, p, p, p, 1, p, p, 1, 1 << 23, 1, 1, 64, 16, 0, None)
     assert rc == _abi.PA_ERR_SHAPE
+    # the fp8 verify entry: packed rows need cu_seqlens, at least one token per sequence
+    ver = [p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, p, 1, 4, p, 1 << 20, p,
+           None]
+    assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_NULL
+    ver[7] = p
+    ver[10] = 1                                           # 1 token for 2 sequences
+    assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_SHAPE
+    ver[10], ver[17] = 4, 0                               # an empty table: a no-op
+    assert L.paged_attn_verify_fp8(*ver) == _abi.PA_OK
     v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, nul, 0, 0, nul, 0,
          nul, nul]
     assert L.paged_attn_varlen_prefill(*v) == _abi.PA_ERR_DTYPE                  # fp32 prefill
