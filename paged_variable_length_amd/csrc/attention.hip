@@ -1138,12 +1138,23 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   // previous iteration finished with; exponentials of j with scores of j+1; value product
   // of j with the mask of j+1. Unrolled by two so buffers and score sets are named
   // statically: even j reads K buffer 1, V buffer 0, keeps scores of j in sa.
+  //
+  // Buffer protocol. K(t) lives in K buffer t%2: its direct loads are issued in iteration t-2
+  // and it is read in iteration t-1 (tile 0: loaded and read in the prologue); V(t) lives in V
+  // buffer t%2, loaded in iteration t-1 and read in iteration t. Every wave passes the
+  // barrier at the top of an iteration only after s_waitcnt(0), i.e. after its own direct
+  // loads have written LDS (vmcnt) and its own LDS reads have returned their data (lgkmcnt).
+  // So once any wave is past the barrier of iteration j, (a) all loads issued before it are
+  // in LDS for every wave, and (b) every read issued before it is complete, and a buffer read
+  // in iteration j-1 can be overwritten. Iteration 0 overwrites K buffer 0, whose tile 0 the
+  // prologue read, so it needs that barrier too whenever it issues K(2) (a wave with no tile
+  // to compute skips the prologue's reads and would otherwise reach the issue first).
   auto iteration = [&](int j, auto par_tag, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
     constexpr int PAR = decltype(par_tag)::value;
     // opaque redefinition: values derived from these bases (the per-k-step and per-piece
     // addresses) are then recomputed where used instead of held in registers across the loop
     asm volatile("" : "+v"(ka0), "+v"(dma0));
-    if (j > 0) {
+    if (j > 0 || ntiles > 2) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
