@@ -216,6 +216,7 @@ class Runner:
         with torch.cuda.stream(self.copy_stream):
             self.dev[k][:n].copy_(self.pin[k][:n], non_blocking=True)
             self.copy_ev[k].record()
+        self.kinds = t.kinds
         return nt, nc, t.num_partials
 
     def write_cache(self):
@@ -242,18 +243,18 @@ class Runner:
         if self.fp8 and self.decode_only:
             pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
                                      v["v_scales"], self.bt, self.ctx, self.scale, tasks,
-                                     combines, nparts, self.ws, self.out)
+                                     self.kinds, combines, nparts, self.ws, self.out)
         elif self.fp8:
             pa.paged_attn_verify_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
                                      v["v_scales"], self.bt, self.cu, self.ctx, self.scale,
-                                     tasks, combines, nparts, self.ws, self.out)
+                                     tasks, self.kinds, combines, nparts, self.ws, self.out)
         elif self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,
-                                 tasks, combines, nparts, self.ws, self.out)
+                                 tasks, self.kinds, combines, nparts, self.ws, self.out)
         else:
             pa.paged_attn_varlen_prefill(v["q"], v["k_pages"], v["v_pages"], self.bt, self.cu,
-                                         self.ctx, self.scale, tasks, combines, nparts, self.ws,
-                                         self.out)
+                                         self.ctx, self.scale, tasks, self.kinds, combines,
+                                         nparts, self.ws, self.out)
         if ev_pair is not None:
             ev_pair[1].record()
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 
 enum pa_status {
   PA_OK = 0,
@@ -75,6 +75,12 @@ enum pa_task_kind {
   PA_TASK_SHARED = 3
 };
 
+/* Bit of a task kind in a `task_kinds` mask: a table's mask holds PA_KIND_BIT(k) for every kind
+ * k among its tasks. build_task_table reports it; every attention entry takes it and refuses
+ * (PA_ERR_INPUT) a table holding a kind that entry does not run, so no output row is silently
+ * left unwritten. */
+#define PA_KIND_BIT(k) (1u << (k))
+
 /* One unit of attention work (8 x int32 = 32 bytes).
  *   kind    PA_TASK_DECODE: the single query row of sequence `seq`, all Hq/Hkv query heads of
  *           kv head `head`, keys [kv0, kv1).
@@ -83,8 +89,8 @@ enum pa_task_kind {
  *           PA_TASK_VERIFY: all q_rows (2..16) rows of a short sequence (a speculative draft
  *           being verified; XY-Serve page, section 2.2, "Meta-Attention" serves prefill,
  *           decode and verify alike) for all Hq/Hkv query heads of kv head `head`, keys
- *           [kv0, kv1) minus the causal mask; q_row0 = 0. Only paged_attn_varlen_prefill runs
- *           these tasks.
+ *           [kv0, kv1) minus the causal mask; q_row0 = 0. paged_attn_varlen_prefill and
+ *           paged_attn_verify_fp8 run these tasks.
  *           PA_TASK_SHARED: keys [kv0, kv1) of a prefix that q_rows consecutive decode
  *           sequences seq .. seq+q_rows-1 hold in the same physical blocks (XY-Serve page,
  *           automatic prefix cache; ATB page, KV cache reuse), for their single query rows and
@@ -156,6 +162,9 @@ int pa_pack_seqlens(const int32_t* lengths, int32_t n, int32_t* cu_seqlens);
  *   with capacity 0 sizes the buffers (then PA_ERR_CAPACITY). balance, if non-NULL, receives
  *   {min/max of per-worker load sums when the sorted tasks are dealt in a snake order,
  *    the same when dealt by i % num_workers} (XY-Serve page, section 4.4, load-balance report).
+ *   task_kinds, if non-NULL, receives the table's kind mask (PA_KIND_BIT of every kind
+ *   emitted; 0 for an empty table or when the buffers are too small), which the attention
+ *   entries take alongside the table.
  *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (heads or tiling parameters), PA_ERR_BLOCK_SIZE,
  *   PA_ERR_INPUT (cu[0] != 0, a q_len < 1, a context shorter than its rows, shared_min > 0
  *   here), PA_ERR_CAPACITY. Pure, deterministic, thread-safe, no HIP calls. */
@@ -163,7 +172,7 @@ int build_task_table(const pa_params* params, const int32_t* cu_seqlens_q_host,
                      const int32_t* context_lens_host, int32_t num_seqs, pa_task* tasks,
                      int32_t tasks_cap, int32_t* num_tasks, pa_combine* combines,
                      int32_t combines_cap, int32_t* num_combines, int32_t* num_partials,
-                     double* balance);
+                     double* balance, uint32_t* task_kinds);
 
 /* build_task_table plus shared-prefix groups, from a host copy of the block table
  * [num_seqs, max_blocks_per_seq] (XY-Serve page, automatic prefix cache; ATB page, KV cache
@@ -191,7 +200,7 @@ int build_task_table_shared(const pa_params* params, const int32_t* cu_seqlens_q
                             const int32_t* block_table_host, int32_t max_blocks_per_seq,
                             pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
                             pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
-                            int32_t* num_partials, double* balance);
+                            int32_t* num_partials, double* balance, uint32_t* task_kinds);
 
 /* Workspace bytes for `num_partials` partial rows of head_dim D (fp32 accumulator row plus
  * running max and sum), rounded up to 256 bytes. 0 when num_partials <= 0. */
@@ -224,15 +233,19 @@ int reshape_and_cache(const void* k_new, const void* v_new, void* k_pages, void*
  *   workspace, out.
  *   workspace: device buffer of at least pa_workspace_bytes(num_partials, D) bytes
  *   (may be NULL when num_partials == 0 and num_combines == 0).
+ *   task_kinds: the table's kind mask from build_task_table; it may hold PA_TASK_DECODE and
+ *   PA_TASK_SHARED only, and must be non-zero when num_tasks > 0.
  *   Errors: PA_ERR_NULL, PA_ERR_SHAPE (Hq % Hkv, Hq/Hkv > 16, D, num_tasks or num_combines
  *   above 8,388,607: one workgroup each), PA_ERR_BLOCK_SIZE, PA_ERR_DTYPE, PA_ERR_CAPACITY
- *   (workspace too small for the partial rows), PA_ERR_HIP. num_tasks == 0 is a no-op. */
+ *   (workspace too small for the partial rows), PA_ERR_INPUT (task_kinds names a kind this
+ *   entry does not run, or is 0 for a non-empty table), PA_ERR_HIP. num_tasks == 0 is a
+ *   no-op. */
 int paged_attn_decode(const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                       int32_t dtype, const pa_task* tasks_dev, int32_t num_tasks,
-                      const pa_combine* combines_dev, int32_t num_combines,
+                      uint32_t task_kinds, const pa_combine* combines_dev, int32_t num_combines,
                       int32_t num_partials, void* workspace, size_t workspace_bytes, void* out,
                       void* stream);
 
@@ -242,7 +255,8 @@ int paged_attn_decode(const void* q, const void* k_pages, const void* v_pages,
  * over an already cached prefix). q [num_tokens, Hq, D] -> out [num_tokens, Hq, D].
  * Decode tasks run the split-K decode path, prefill tasks the bf16 MFMA tile path, both inside
  * one grid in table order; then split partials are merged.
- *   dtype must be PA_BF16 (the prefill path runs on bf16 MFMA).
+ *   dtype must be PA_BF16 (the prefill path runs on bf16 MFMA). task_kinds may hold every
+ *   kind (this entry runs them all).
  *   Errors as paged_attn_decode, plus PA_ERR_SHAPE for num_tokens < num_seqs and
  *   PA_ERR_DTYPE for any dtype other than PA_BF16. */
 int paged_attn_varlen_prefill(const void* q, const void* k_pages, const void* v_pages,
@@ -251,7 +265,8 @@ int paged_attn_varlen_prefill(const void* q, const void* k_pages, const void* v_
                               int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               float scale, int32_t dtype, const pa_task* tasks_dev,
-                              int32_t num_tasks, const pa_combine* combines_dev,
+                              int32_t num_tasks, uint32_t task_kinds,
+                              const pa_combine* combines_dev,
                               int32_t num_combines, int32_t num_partials, void* workspace,
                               size_t workspace_bytes, void* out, void* stream);
 
@@ -277,16 +292,16 @@ int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages, v
                           int32_t block_size, void* stream);
 
 /* Decode attention over fp8 pages: as paged_attn_decode with dtype PA_BF16 for q and out, each
- * cached value read as code * page scale (an exact bf16 value, converted on load). The task
- * table is one built with verify_rows = 0: the kernel runs PA_TASK_DECODE and PA_TASK_SHARED
- * tasks, and the outputs of any other kind are not written. Errors as paged_attn_decode. */
+ * cached value read as code * page scale (an exact bf16 value, converted on load). The kernel
+ * runs PA_TASK_DECODE and PA_TASK_SHARED tasks: task_kinds may hold those two only (a table
+ * built with verify_rows = 0 from one-row sequences). Errors as paged_attn_decode. */
 int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
                           const float* k_scales, const float* v_scales,
                           const int32_t* block_table, int32_t max_blocks_per_seq,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           float scale, const pa_task* tasks_dev, int32_t num_tasks,
-                          const pa_combine* combines_dev, int32_t num_combines,
+                          uint32_t task_kinds, const pa_combine* combines_dev, int32_t num_combines,
                           int32_t num_partials, void* workspace, size_t workspace_bytes,
                           void* out, void* stream);
 
@@ -296,7 +311,8 @@ int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_page
  * q and out bf16 [num_tokens, Hq, D] packed by cu_seqlens_q, with the pages, scales and value
  * reading of paged_attn_decode_fp8. Runs the PA_TASK_DECODE and PA_TASK_VERIFY tasks of the table
  * (built with verify_rows > 0): each verify row sees the keys up to and including its own
- * position. Prefill and shared-prefix tasks are not run and their outputs are not written.
+ * position. task_kinds may hold PA_TASK_DECODE and PA_TASK_VERIFY only (prefill and
+ * shared-prefix tasks are refused with PA_ERR_INPUT).
  *   Device pointers: q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
  *   context_lens, tasks_dev, combines_dev, workspace, out.
  *   Errors as paged_attn_decode_fp8, plus PA_ERR_SHAPE for num_tokens < num_seqs. */
@@ -307,9 +323,9 @@ int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_page
                           int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           float scale, const pa_task* tasks_dev, int32_t num_tasks,
-                          const pa_combine* combines_dev, int32_t num_combines,
-                          int32_t num_partials, void* workspace, size_t workspace_bytes,
-                          void* out, void* stream);
+                          uint32_t task_kinds, const pa_combine* combines_dev,
+                          int32_t num_combines, int32_t num_partials, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream);
 
 /* Debug check of a host copy of a block table (cann-recipes-infer page, section 4.4, first
  * check: page ids inside [0, max_pages)): every entry a sequence needs,

@@ -69,6 +69,7 @@ class TaskTable:
     num_partials: int
     balance_snake: float
     balance_modulo: float
+    kinds: int               # PA_KIND_BIT mask of the task kinds present
 
 
 def build_task_table(params: PaParams, cu_seqlens_q, context_lens, tasks_out=None,
@@ -95,10 +96,11 @@ def build_task_table(params: PaParams, cu_seqlens_q, context_lens, tasks_out=Non
         fn, name, head = L.build_task_table_shared, "build_task_table_shared", \
             [_ptr(bt), bt.shape[1]]
     nt, nc, npart = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    kinds = ctypes.c_uint32(0)
     bal = (ctypes.c_double * 2)() if with_balance else None
     if tasks_out is None:
         rc = fn(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, *head, None, 0, ctypes.byref(nt),
-                None, 0, ctypes.byref(nc), ctypes.byref(npart), None)
+                None, 0, ctypes.byref(nc), ctypes.byref(npart), None, None)
         if rc not in (_abi.PA_OK, _abi.PA_ERR_CAPACITY):
             check(rc, name)
         tasks_out = np.zeros((nt.value, 8), dtype=np.int32)
@@ -109,11 +111,12 @@ def build_task_table(params: PaParams, cu_seqlens_q, context_lens, tasks_out=Non
     rc = fn(ctypes.byref(params), _ptr(cu), _ptr(ctx), n, *head,
             tasks_out.ctypes.data_as(ctypes.POINTER(PaTask)), tasks_out.shape[0],
             ctypes.byref(nt), combines_out.ctypes.data_as(ctypes.POINTER(PaCombine)),
-            combines_out.shape[0], ctypes.byref(nc), ctypes.byref(npart), bal)
+            combines_out.shape[0], ctypes.byref(nc), ctypes.byref(npart), bal,
+            ctypes.byref(kinds))
     check(rc, name)
     return TaskTable(tasks_out[:nt.value], combines_out[:nc.value], npart.value,
                      bal[0] if bal is not None else float("nan"),
-                     bal[1] if bal is not None else float("nan"))
+                     bal[1] if bal is not None else float("nan"), kinds.value)
 
 
 def workspace_bytes(num_partials: int, head_dim: int) -> int:
@@ -228,7 +231,7 @@ def _attn_common(q, k_pages, v_pages, block_table, context_lens, out):
             _dev(block_table, "block_table", torch.int32), block_table.shape[1]]
 
 
-def _table_args(tasks_dev, combines_dev, num_partials, workspace):
+def _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace):
     torch = _torch()
     _dev(tasks_dev, "tasks_dev", torch.int32, 2)
     if combines_dev.shape[0] > 0:
@@ -238,15 +241,16 @@ def _table_args(tasks_dev, combines_dev, num_partials, workspace):
     if workspace is not None and workspace.numel() > 0:
         ws = _dev(workspace, "workspace")
         wsb = workspace.numel() * workspace.element_size()
-    return [ctypes.c_void_p(tasks_dev.data_ptr()), tasks_dev.shape[0],
+    return [ctypes.c_void_p(tasks_dev.data_ptr()), tasks_dev.shape[0], int(task_kinds),
             ctypes.c_void_p(combines_dev.data_ptr() if combines_dev.numel() else 0),
             combines_dev.shape[0], int(num_partials), ws, wsb]
 
 
 def paged_attn_decode(q, k_pages, v_pages, block_table, context_lens, scale, tasks_dev,
-                      combines_dev, num_partials, workspace, out, stream=None):
+                      task_kinds, combines_dev, num_partials, workspace, out, stream=None):
     """Decode attention (library kernels). q/out [N, Hq, D]; tasks from a table built with
-    cu_seqlens = 0..N, copied to the device as int32 [n, 8]."""
+    cu_seqlens = 0..N, copied to the device as int32 [n, 8]; task_kinds is the table's kind
+    mask (TaskTable.kinds)."""
     torch = _torch()
     head = _attn_common(q, k_pages, v_pages, block_table, context_lens, out)
     n, hq, d = q.shape
@@ -254,14 +258,14 @@ def paged_attn_decode(q, k_pages, v_pages, block_table, context_lens, scale, tas
         raise ValueError("decode takes one query row per sequence")
     args = head + [_dev(context_lens, "context_lens", torch.int32), n, hq, k_pages.shape[1], d,
                    k_pages.shape[2], float(scale), _dtype_code(q)] + \
-        _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out"), _stream(stream)]
     check(lib().paged_attn_decode(*args), "paged_attn_decode")
 
 
 def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, context_lens,
-                          scale, tasks_dev, combines_dev, num_partials, workspace, out,
-                          stream=None):
+                          scale, tasks_dev, task_kinds, combines_dev, num_partials, workspace,
+                          out, stream=None):
     """Decode attention over fp8 pages with page scales (library kernels). q/out bf16
     [N, Hq, D]; pages uint8 [NB, Hkv, bs, D]; scales float32 [NB, Hkv]."""
     torch = _torch()
@@ -280,14 +284,15 @@ def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, 
             _dev(v_scales, "v_scales", torch.float32),
             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
             _dev(context_lens, "context_lens", torch.int32), n, hq, hkv, d, k_pages.shape[2],
-            float(scale)] + _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+            float(scale)] + \
+        _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out", torch.bfloat16), _stream(stream)]
     check(lib().paged_attn_decode_fp8(*args), "paged_attn_decode_fp8")
 
 
 def paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
-                          context_lens, scale, tasks_dev, combines_dev, num_partials, workspace,
-                          out, stream=None):
+                          context_lens, scale, tasks_dev, task_kinds, combines_dev, num_partials,
+                          workspace, out, stream=None):
     """Decode rows and speculative drafts over fp8 pages with page scales (library kernels).
     q/out bf16 [T, Hq, D] packed by cu_seqlens_q; pages uint8 [NB, Hkv, bs, D]; scales
     float32 [NB, Hkv]. Runs the table's decode and verify tasks only."""
@@ -309,14 +314,15 @@ def paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, 
             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
             _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
             _dev(context_lens, "context_lens", torch.int32), n, t, hq, hkv, d, k_pages.shape[2],
-            float(scale)] + _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+            float(scale)] + \
+        _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out", torch.bfloat16), _stream(stream)]
     check(lib().paged_attn_verify_fp8(*args), "paged_attn_verify_fp8")
 
 
 def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
-                              scale, tasks_dev, combines_dev, num_partials, workspace, out,
-                              stream=None):
+                              scale, tasks_dev, task_kinds, combines_dev, num_partials, workspace,
+                              out, stream=None):
     """Packed causal attention over paged prefixes, decode rows and prefill chunks mixed
     (library kernels). q/out [T, Hq, D]."""
     torch = _torch()
@@ -328,7 +334,7 @@ def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, co
     args = head + [_dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
                    _dev(context_lens, "context_lens", torch.int32), n, T, hq, k_pages.shape[1],
                    d, k_pages.shape[2], float(scale), _dtype_code(q)] + \
-        _table_args(tasks_dev, combines_dev, num_partials, workspace) + \
+        _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out"), _stream(stream)]
     check(lib().paged_attn_varlen_prefill(*args), "paged_attn_varlen_prefill")
 
@@ -375,7 +381,8 @@ class StepPlan:
     def decode(self, q, k_pages, v_pages, scale, out, stream=None):
         self._check_decode_table("decode")
         paged_attn_decode(q, k_pages, v_pages, self.block_table, self.ctx, scale, self.tasks,
-                          self.combines, self.num_partials, self.workspace, out, stream)
+                          self.table.kinds, self.combines, self.num_partials, self.workspace, out,
+                          stream)
 
     def write_cache_fp8(self, k_new, v_new, k_pages, v_pages, k_scales, v_scales, stream=None):
         reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, k_scales, v_scales,
@@ -384,8 +391,8 @@ class StepPlan:
     def decode_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
         self._check_decode_table("decode_fp8")
         paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table,
-                              self.ctx, scale, self.tasks, self.combines, self.num_partials,
-                              self.workspace, out, stream)
+                              self.ctx, scale, self.tasks, self.table.kinds, self.combines,
+                              self.num_partials, self.workspace, out, stream)
 
     def verify_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
         kinds = set(np.unique(self.table.tasks[:, 0]).tolist()) if len(self.table.tasks) else set()
@@ -393,13 +400,13 @@ class StepPlan:
             raise ValueError("verify_fp8 runs decode and verify tasks only: build the table with "
                              "verify_rows covering every draft and shared_min 0")
         paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table, self.cu,
-                              self.ctx, scale, self.tasks, self.combines, self.num_partials,
-                              self.workspace, out, stream)
+                              self.ctx, scale, self.tasks, self.table.kinds, self.combines,
+                              self.num_partials, self.workspace, out, stream)
 
     def varlen(self, q, k_pages, v_pages, scale, out, stream=None):
         paged_attn_varlen_prefill(q, k_pages, v_pages, self.block_table, self.cu, self.ctx,
-                                  scale, self.tasks, self.combines, self.num_partials,
-                                  self.workspace, out, stream)
+                                  scale, self.tasks, self.table.kinds, self.combines,
+                                  self.num_partials, self.workspace, out, stream)
 
 
 # ------------------------------------------------------------------ SmoothGEMM

@@ -25,7 +25,8 @@ PA_TASK_DECODE = 0
 PA_TASK_PREFILL = 1
 PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
-ABI_VERSION = 7
+ALL_KINDS = 0xF          # PA_KIND_BIT of every task kind
+ABI_VERSION = 8
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m paged_variable_length_amd.build` (no fallback exists)")
     L = ctypes.CDLL(LIB_PATH)
-    i32, p = ctypes.c_int32, ctypes.c_void_p
+    i32, u32, p = ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
     pi32 = ctypes.POINTER(ctypes.c_int32)
     L.pa_abi_version.restype = ctypes.c_int
     L.pa_abi_version.argtypes = []
@@ -100,15 +101,16 @@ def lib() -> ctypes.CDLL:
     L.pa_pack_seqlens.restype = ctypes.c_int
     L.pa_pack_seqlens.argtypes = [pi32, i32, pi32]
     L.build_task_table.restype = ctypes.c_int
+    pu32 = ctypes.POINTER(ctypes.c_uint32)
     L.build_task_table.argtypes = [ctypes.POINTER(PaParams), pi32, pi32, i32,
                                    ctypes.POINTER(PaTask), i32, pi32,
                                    ctypes.POINTER(PaCombine), i32, pi32, pi32,
-                                   ctypes.POINTER(ctypes.c_double)]
+                                   ctypes.POINTER(ctypes.c_double), pu32]
     L.build_task_table_shared.restype = ctypes.c_int
     L.build_task_table_shared.argtypes = [ctypes.POINTER(PaParams), pi32, pi32, i32, pi32, i32,
                                           ctypes.POINTER(PaTask), i32, pi32,
                                           ctypes.POINTER(PaCombine), i32, pi32, pi32,
-                                          ctypes.POINTER(ctypes.c_double)]
+                                          ctypes.POINTER(ctypes.c_double), pu32]
     L.pa_workspace_bytes.restype = ctypes.c_size_t
     L.pa_workspace_bytes.argtypes = [i32, i32]
     L.reshape_and_cache.restype = ctypes.c_int
@@ -116,22 +118,22 @@ def lib() -> ctypes.CDLL:
                                     i32, p]
     L.paged_attn_decode.restype = ctypes.c_int
     L.paged_attn_decode.argtypes = [p, p, p, p, i32, p, i32, i32, i32, i32, i32,
-                                    ctypes.c_float, i32, p, i32, p, i32, i32, p,
+                                    ctypes.c_float, i32, p, i32, u32, p, i32, i32, p,
                                     ctypes.c_size_t, p, p]
     L.paged_attn_varlen_prefill.restype = ctypes.c_int
     L.paged_attn_varlen_prefill.argtypes = [p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
-                                            i32, ctypes.c_float, i32, p, i32, p, i32, i32, p,
-                                            ctypes.c_size_t, p, p]
+                                            i32, ctypes.c_float, i32, p, i32, u32, p, i32, i32,
+                                            p, ctypes.c_size_t, p, p]
     L.reshape_and_cache_fp8.restype = ctypes.c_int
     L.reshape_and_cache_fp8.argtypes = [p, p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                         i32, p]
     L.paged_attn_decode_fp8.restype = ctypes.c_int
     L.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
-                                        ctypes.c_float, p, i32, p, i32, i32, p, ctypes.c_size_t,
-                                        p, p]
+                                        ctypes.c_float, p, i32, u32, p, i32, i32, p,
+                                        ctypes.c_size_t, p, p]
     L.paged_attn_verify_fp8.restype = ctypes.c_int
     L.paged_attn_verify_fp8.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
-                                        i32, ctypes.c_float, p, i32, p, i32, i32, p,
+                                        i32, ctypes.c_float, p, i32, u32, p, i32, i32, p,
                                         ctypes.c_size_t, p, p]
     L.pa_validate_block_table.restype = ctypes.c_int
     L.pa_validate_block_table.argtypes = [pi32, i32, pi32, i32, i32, i32]

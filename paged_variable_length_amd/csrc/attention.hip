@@ -1468,6 +1468,23 @@ int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hk
   return PA_OK;
 }
 
+// The table's kind mask against the kinds this entry runs: a kind outside `allowed` would be
+// skipped by the kernel and leave its rows of `out` unwritten, so it is refused here.
+int check_kinds(const char* who, int32_t num_tasks, uint32_t kinds, uint32_t allowed) {
+  if (num_tasks > 0 && kinds == 0)
+    return pa::set_error(PA_ERR_INPUT, "%s: task_kinds is 0 for a table of %d tasks", who,
+                         num_tasks);
+  if (kinds & ~allowed)
+    return pa::set_error(PA_ERR_INPUT, "%s: the table holds task kinds 0x%x; this entry runs 0x%x",
+                         who, kinds, allowed);
+  return PA_OK;
+}
+
+constexpr uint32_t kAllKinds = PA_KIND_BIT(PA_TASK_DECODE) | PA_KIND_BIT(PA_TASK_PREFILL) |
+                               PA_KIND_BIT(PA_TASK_VERIFY) | PA_KIND_BIT(PA_TASK_SHARED);
+constexpr uint32_t kDecodeKinds = PA_KIND_BIT(PA_TASK_DECODE) | PA_KIND_BIT(PA_TASK_SHARED);
+constexpr uint32_t kVerifyKinds = PA_KIND_BIT(PA_TASK_DECODE) | PA_KIND_BIT(PA_TASK_VERIFY);
+
 AttnArgs make_args(const void* q, const void* kp, const void* vp, const int32_t* bt,
                    int32_t max_blocks, const int32_t* cu, const int32_t* ctx, int32_t hq,
                    int32_t hkv, int32_t d, int32_t bs, float scale, const pa_task* tasks,
@@ -1552,13 +1569,14 @@ extern "C" int paged_attn_decode(const void* q, const void* k_pages, const void*
                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, float scale, int32_t dtype,
                                  const pa_task* tasks_dev, int32_t num_tasks,
-                                 const pa_combine* combines_dev, int32_t num_combines,
-                                 int32_t num_partials, void* workspace, size_t workspace_bytes,
-                                 void* out, void* stream) {
+                                 uint32_t task_kinds, const pa_combine* combines_dev,
+                                 int32_t num_combines, int32_t num_partials, void* workspace,
+                                 size_t workspace_bytes, void* out, void* stream) {
   if (int rc = check_attn_scalars("paged_attn_decode", num_seqs, num_q_heads, num_kv_heads,
                                   head_dim, block_size, dtype, num_tasks, num_combines,
                                   num_partials, workspace_bytes, workspace, max_blocks_per_seq))
     return rc;
+  if (int rc = check_kinds("paged_attn_decode", num_tasks, task_kinds, kDecodeKinds)) return rc;
   if (num_tasks == 0) return pa::clear_error();
   if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out || !tasks_dev ||
       (num_combines > 0 && !combines_dev))
@@ -1592,12 +1610,15 @@ extern "C" int paged_attn_varlen_prefill(
     int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* context_lens,
     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float scale, int32_t dtype, const pa_task* tasks_dev,
-    int32_t num_tasks, const pa_combine* combines_dev, int32_t num_combines,
-    int32_t num_partials, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+    int32_t num_tasks, uint32_t task_kinds, const pa_combine* combines_dev,
+    int32_t num_combines, int32_t num_partials, void* workspace, size_t workspace_bytes,
+    void* out, void* stream) {
   if (int rc = check_attn_scalars("paged_attn_varlen_prefill", num_seqs, num_q_heads,
                                   num_kv_heads, head_dim, block_size, dtype, num_tasks,
                                   num_combines, num_partials, workspace_bytes, workspace,
                                   max_blocks_per_seq))
+    return rc;
+  if (int rc = check_kinds("paged_attn_varlen_prefill", num_tasks, task_kinds, kAllKinds))
     return rc;
   if (dtype != PA_BF16)
     return pa::set_error(PA_ERR_DTYPE, "paged_attn_varlen_prefill: the MFMA path needs PA_BF16");
@@ -1671,12 +1692,15 @@ extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const v
                                      int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, float scale,
                                      const pa_task* tasks_dev, int32_t num_tasks,
-                                     const pa_combine* combines_dev, int32_t num_combines,
-                                     int32_t num_partials, void* workspace,
-                                     size_t workspace_bytes, void* out, void* stream) {
+                                     uint32_t task_kinds, const pa_combine* combines_dev,
+                                     int32_t num_combines, int32_t num_partials,
+                                     void* workspace, size_t workspace_bytes, void* out,
+                                     void* stream) {
   if (int rc = check_attn_scalars("paged_attn_decode_fp8", num_seqs, num_q_heads, num_kv_heads,
                                   head_dim, block_size, PA_BF16, num_tasks, num_combines,
                                   num_partials, workspace_bytes, workspace, max_blocks_per_seq))
+    return rc;
+  if (int rc = check_kinds("paged_attn_decode_fp8", num_tasks, task_kinds, kDecodeKinds))
     return rc;
   if (num_tasks == 0) return pa::clear_error();
   if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !context_lens ||
@@ -1705,12 +1729,15 @@ extern "C" int paged_attn_verify_fp8(const void* q, const void* k_pages, const v
                                      int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                      float scale, const pa_task* tasks_dev, int32_t num_tasks,
-                                     const pa_combine* combines_dev, int32_t num_combines,
-                                     int32_t num_partials, void* workspace,
-                                     size_t workspace_bytes, void* out, void* stream) {
+                                     uint32_t task_kinds, const pa_combine* combines_dev,
+                                     int32_t num_combines, int32_t num_partials,
+                                     void* workspace, size_t workspace_bytes, void* out,
+                                     void* stream) {
   if (int rc = check_attn_scalars("paged_attn_verify_fp8", num_seqs, num_q_heads, num_kv_heads,
                                   head_dim, block_size, PA_BF16, num_tasks, num_combines,
                                   num_partials, workspace_bytes, workspace, max_blocks_per_seq))
+    return rc;
+  if (int rc = check_kinds("paged_attn_verify_fp8", num_tasks, task_kinds, kVerifyKinds))
     return rc;
   if (num_tokens < num_seqs)
     return pa::set_error(PA_ERR_SHAPE, "paged_attn_verify_fp8: %d tokens for %d sequences",

@@ -332,7 +332,7 @@ int check_table_inputs(const pa_params* p, const int32_t* cu, const int32_t* ctx
 int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
                 const int32_t* pair, pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
                 pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
-                int32_t* num_partials, double* balance);
+                int32_t* num_partials, double* balance, uint32_t* task_kinds);
 
 }  // namespace
 
@@ -340,14 +340,15 @@ int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32
 extern "C" int build_task_table(const pa_params* p, const int32_t* cu, const int32_t* ctx,
                                 int32_t num_seqs, pa_task* tasks, int32_t tasks_cap,
                                 int32_t* num_tasks, pa_combine* combines, int32_t combines_cap,
-                                int32_t* num_combines, int32_t* num_partials, double* balance) {
+                                int32_t* num_combines, int32_t* num_partials, double* balance,
+                                uint32_t* task_kinds) {
   if (int rc = check_table_inputs(p, cu, ctx, num_seqs, num_tasks, num_combines, num_partials))
     return rc;
   if (p->shared_min > 0)
     return set_error(PA_ERR_INPUT,
                      "shared_min > 0 needs the block table: call build_task_table_shared");
   return build_table(p, cu, ctx, num_seqs, nullptr, tasks, tasks_cap, num_tasks, combines,
-                     combines_cap, num_combines, num_partials, balance);
+                     combines_cap, num_combines, num_partials, balance, task_kinds);
 }
 
 // The same plus shared-prefix groups (XY-Serve page, automatic prefix cache; ATB page, KV cache
@@ -357,12 +358,12 @@ extern "C" int build_task_table_shared(const pa_params* p, const int32_t* cu, co
                                        pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
                                        pa_combine* combines, int32_t combines_cap,
                                        int32_t* num_combines, int32_t* num_partials,
-                                       double* balance) {
+                                       double* balance, uint32_t* task_kinds) {
   if (int rc = check_table_inputs(p, cu, ctx, num_seqs, num_tasks, num_combines, num_partials))
     return rc;
   if (p->shared_min == 0)
     return build_table(p, cu, ctx, num_seqs, nullptr, tasks, tasks_cap, num_tasks, combines,
-                       combines_cap, num_combines, num_partials, balance);
+                       combines_cap, num_combines, num_partials, balance, task_kinds);
   if (num_seqs > 0 && !bt)
     return set_error(PA_ERR_NULL, "build_task_table_shared: block_table is NULL");
   const int32_t bs = p->block_size;
@@ -389,7 +390,7 @@ extern "C" int build_task_table_shared(const pa_params* p, const int32_t* cu, co
     pair[s] = static_cast<int32_t>(int64_t(common) * bs / pa::kSplitQuantum * pa::kSplitQuantum);
   }
   return build_table(p, cu, ctx, num_seqs, pair.data(), tasks, tasks_cap, num_tasks, combines,
-                     combines_cap, num_combines, num_partials, balance);
+                     combines_cap, num_combines, num_partials, balance, task_kinds);
 }
 
 namespace {
@@ -397,7 +398,7 @@ namespace {
 int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
                 const int32_t* pair, pa_task* tasks, int32_t tasks_cap, int32_t* num_tasks,
                 pa_combine* combines, int32_t combines_cap, int32_t* num_combines,
-                int32_t* num_partials, double* balance) {
+                int32_t* num_partials, double* balance, uint32_t* task_kinds) {
   int64_t nt = 0, nc = 0, np = 0;
   count(p, cu, ctx, num_seqs, pair, &nt, &nc, &np);
   if (nt > INT32_MAX || nc > INT32_MAX || np > INT32_MAX)
@@ -405,6 +406,7 @@ int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32
   *num_tasks = static_cast<int32_t>(nt);
   *num_combines = static_cast<int32_t>(nc);
   *num_partials = static_cast<int32_t>(np);
+  if (task_kinds) *task_kinds = 0;
   if (nt > tasks_cap || nc > combines_cap) {
     if (balance) balance[0] = balance[1] = 0.0;
     return set_error(PA_ERR_CAPACITY, "need %lld tasks (cap %d) and %lld combines (cap %d)",
@@ -425,6 +427,7 @@ int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32
   pa_task* emitted = sc.task.data();
   int64_t nti = 0, nci = 0, parts = 0;
   int64_t mn = INT64_MAX, mx = 0;
+  uint32_t kinds = 0;
   decompose(
       p, cu, ctx, num_seqs, pair,
       [&](int64_t load, const pa_task& t) {
@@ -433,6 +436,7 @@ int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32
           emitted[nti] = t;
           mn = std::min(mn, load);
           mx = std::max(mx, load);
+          kinds |= 1u << t.kind;
         }
         ++nti;
       },
@@ -457,6 +461,7 @@ int build_table(const pa_params* p, const int32_t* cu, const int32_t* ctx, int32
     order = idx;
   }
   for (int64_t i = 0; i < nt; ++i) tasks[i] = emitted[static_cast<uint32_t>(order[i])];
+  if (task_kinds) *task_kinds = kinds;
   if (balance) {
     const int32_t W = p->num_workers;
     std::vector<int64_t> snake(W, 0), modulo(W, 0);

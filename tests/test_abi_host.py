@@ -53,7 +53,16 @@ def compare_tables(q_lens, ctx, **kw):
     assert got.num_partials == ref_np
     assert got.balance_snake == ref_bal["snake"]
     assert got.balance_modulo == ref_bal["modulo"]
+    assert got.kinds == kind_mask(ref_t)
     return got
+
+
+def kind_mask(tasks):
+    """PA_KIND_BIT mask of the kinds among task records (column 0)."""
+    m = 0
+    for k in set(np.asarray(tasks)[:, 0].tolist()):
+        m |= 1 << int(k)
+    return m
 
 
 @pytest.mark.parametrize("name", ["tiny_decode_fp32", "decode_mha_bf16", "decode_gqa_bf16_bs16",
@@ -143,7 +152,7 @@ def test_task_table_capacity_sizing():
     P = ctypes.POINTER(ctypes.c_int32)
     rc = L.build_task_table(ctypes.byref(p), cu.ctypes.data_as(P), ctx.ctypes.data_as(P), 1,
                             None, 0, ctypes.byref(nt), None, 0, ctypes.byref(nc),
-                            ctypes.byref(npart), None)
+                            ctypes.byref(npart), None, None)
     assert rc == _abi.PA_ERR_CAPACITY
     assert (nt.value, nc.value, npart.value) == (4, 1, 8)
 
@@ -193,8 +202,8 @@ def test_launcher_scalar_errors_need_no_gpu():
     rc = L.reshape_and_cache(nul, nul, nul, nul, nul, 1, nul, nul, 1, 0, 1, 1, 64, 16, 0, nul)
     assert rc == _abi.PA_OK
     args = lambda hq, hkv, d, bs, dt, ncomb=0, ws=None, wsb=0: [  # noqa: E731
-        nul, nul, nul, nul, 1, nul, 1, hq, hkv, d, bs, 0.1, dt, nul, 1, nul, ncomb, 8, ws, wsb,
-        nul, nul]
+        nul, nul, nul, nul, 1, nul, 1, hq, hkv, d, bs, 0.1, dt, nul, 1, 1, nul, ncomb, 8, ws,
+        wsb, nul, nul]
     assert L.paged_attn_decode(*args(3, 2, 64, 16, 0)) == _abi.PA_ERR_SHAPE
     assert L.paged_attn_decode(*args(34, 1, 64, 16, 0)) == _abi.PA_ERR_SHAPE     # G > 16
     assert L.paged_attn_decode(*args(2, 1, 64, 16, 7)) == _abi.PA_ERR_DTYPE
@@ -209,7 +218,7 @@ def test_launcher_scalar_errors_need_no_gpu():
     assert b"NULL pointer" in L.pa_last_error()
     # every device pointer but context_lens given: still refused before any launch
     p = ctypes.c_void_p(256)
-    full = [p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, 0, p, 1, p, 1, 8, p, 1 << 20, p, None]
+    full = [p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, 0, p, 1, 1, p, 1, 8, p, 1 << 20, p, None]
     assert L.paged_attn_decode(*full) == _abi.PA_ERR_NULL
     fp8 = full[:3] + [p, p] + full[3:12] + full[13:]
     assert L.paged_attn_decode_fp8(*fp8) == _abi.PA_ERR_NULL
@@ -221,17 +230,69 @@ def test_launcher_scalar_errors_need_no_gpu():
     rc = L.reshape_and_cache(p, p, p, p, p, 1, p, p, 1, 1 << 23, 1, 1, 64, 16, 0, None)
     assert rc == _abi.PA_ERR_SHAPE
     # the fp8 verify entry: packed rows need cu_seqlens, at least one token per sequence
-    ver = [p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, p, 1, 4, p, 1 << 20, p,
-           None]
+    ver = [p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, 1, p, 1, 4, p, 1 << 20,
+           p, None]
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_NULL
     ver[7] = p
     ver[10] = 1                                           # 1 token for 2 sequences
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_SHAPE
     ver[10], ver[17] = 4, 0                               # an empty table: a no-op
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_OK
-    v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, nul, 0, 0, nul, 0,
-         nul, nul]
+    v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, 1, nul, 0, 0, nul,
+         0, nul, nul]
     assert L.paged_attn_varlen_prefill(*v) == _abi.PA_ERR_DTYPE                  # fp32 prefill
+
+
+def test_attention_entries_refuse_task_kinds_they_do_not_run():
+    """Each attention entry takes the table's kind mask and refuses, before any HIP call, a
+    table holding a kind its kernel would skip (those rows of `out` would stay unwritten). An
+    accepted mask gets past that check and stops at the NULL pointer left in each call, so no
+    kernel is launched here."""
+    L = _abi.lib()
+    p = ctypes.c_void_p(256)
+    DEC, PRE, VER, SHA = (1 << _abi.PA_TASK_DECODE, 1 << _abi.PA_TASK_PREFILL,
+                          1 << _abi.PA_TASK_VERIFY, 1 << _abi.PA_TASK_SHARED)
+
+    def decode(kinds):      # context_lens NULL
+        return L.paged_attn_decode(p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, 0, p, 1, kinds, p,
+                                   1, 8, p, 1 << 20, p, None)
+
+    def decode_fp8(kinds):  # context_lens NULL
+        return L.paged_attn_decode_fp8(p, p, p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, p, 1,
+                                       kinds, p, 1, 8, p, 1 << 20, p, None)
+
+    def verify_fp8(kinds):  # cu_seqlens NULL
+        return L.paged_attn_verify_fp8(p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p,
+                                       3, kinds, p, 1, 4, p, 1 << 20, p, None)
+
+    def varlen(kinds):      # context_lens NULL
+        return L.paged_attn_varlen_prefill(p, p, p, p, 1, p, None, 1, 2, 2, 1, 64, 16, 0.1, 0, p,
+                                           1, kinds, p, 1, 8, p, 1 << 20, p, None)
+
+    cases = [(decode, DEC | SHA), (decode_fp8, DEC | SHA), (verify_fp8, DEC | VER),
+             (varlen, DEC | PRE | VER | SHA)]
+    for fn, allowed in cases:
+        for kinds in range(1, 16):
+            rc = fn(kinds)
+            if kinds & ~allowed:
+                assert rc == _abi.PA_ERR_INPUT, (fn.__name__, kinds)
+                assert b"task kinds" in L.pa_last_error()
+            else:
+                assert rc == _abi.PA_ERR_NULL, (fn.__name__, kinds)
+        assert fn(0) == _abi.PA_ERR_INPUT                     # no mask for a non-empty table
+        assert fn(1 << 7) == _abi.PA_ERR_INPUT                # not a kind
+    # a real table: a prefill chunk among decode rows cannot go through the decode entry
+    t = pa.build_task_table(pa.make_params(8, 2, 64, 16), pa.pack_seqlens([1, 40, 1]),
+                            np.array([70, 100, 5], np.int32))
+    assert t.kinds == DEC | PRE
+    assert decode(t.kinds) == _abi.PA_ERR_INPUT
+    assert varlen(t.kinds) == _abi.PA_ERR_NULL
+    # verify rows need the verify entry (or the unified one), not the fp8 decode entry
+    t = pa.build_task_table(pa.make_params(8, 2, 64, 16, verify_rows=4),
+                            pa.pack_seqlens([1, 3]), np.array([70, 100], np.int32))
+    assert t.kinds == DEC | VER
+    assert decode_fp8(t.kinds) == _abi.PA_ERR_INPUT
+    assert verify_fp8(t.kinds) == _abi.PA_ERR_NULL
 
 
 def test_binding_refuses_host_tensors():
@@ -271,6 +332,7 @@ def compare_shared(q_lens, ctx, bt, **kw):
     assert got.num_partials == ref_np
     assert got.balance_snake == ref_bal["snake"]
     assert got.balance_modulo == ref_bal["modulo"]
+    assert got.kinds == kind_mask(ref_t)
     return got
 
 
@@ -326,7 +388,7 @@ def test_shared_table_errors():
     rc = L.build_task_table_shared(ctypes.byref(p), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                    ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, None, 8,
                                    None, 0, ctypes.byref(nt), None, 0, ctypes.byref(nc),
-                                   ctypes.byref(npart), None)
+                                   ctypes.byref(npart), None, None)
     assert rc == _abi.PA_ERR_NULL
     # shared_min 0: the plain table, block table or not
     plain = pa.build_task_table(pa.make_params(2, 1, 64, 16), cu, ctx)

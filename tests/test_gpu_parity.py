@@ -361,6 +361,6 @@ def test_empty_table_is_a_no_op():
     pa.paged_attn_decode(vals["q"], vals["k_pages"], vals["v_pages"],
                          torch.from_numpy(w.block_table).to(DEV),
                          torch.from_numpy(w.ctx_lens.astype(np.int32)).to(DEV), 0.125, empty,
-                         empty, 0, None, out)
+                         0, empty, 0, None, out)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
