@@ -11,6 +11,7 @@ import pytest
 
 import synth
 import paged_variable_length_amd as pa
+from bench import TILING as BENCH_TILING
 from paged_variable_length_amd import _abi
 from oracle import task_table as ot
 from tests.helpers import aliased_batch
@@ -72,6 +73,21 @@ def test_task_table_bit_exact_on_workloads(name):
     tiling = dict(dec_split=512, pf_q_tile=128, pf_kv_split=0 if name != "mixed_bf16" else 8192)
     compare_tables(w.q_lens, w.ctx_lens, hq=w.num_q_heads, hkv=w.num_kv_heads, d=w.head_dim,
                    bs=w.block_size, num_workers=512, **tiling)
+
+
+@pytest.mark.parametrize("name", sorted(BENCH_TILING))
+def test_task_table_bit_exact_in_bench_tilings(name):
+    """Every workload bench.py times, in the tiling it times (its TILING, with the 512
+    resident workgroups it reports balance for): the C++ table equals the oracle's bit for bit,
+    shared-prefix groups included."""
+    w = synth.make_workload(name.split(":")[0])
+    tiling = dict(BENCH_TILING[name], num_workers=512)
+    args = dict(hq=w.num_q_heads, hkv=w.num_kv_heads, d=w.head_dim, bs=w.block_size, **tiling)
+    if tiling.get("shared_min"):
+        got = compare_shared(w.q_lens, w.ctx_lens, w.block_table, **args)
+    else:
+        got = compare_tables(w.q_lens, w.ctx_lens, **args)
+    assert len(got.tasks) > 0
 
 
 @pytest.mark.parametrize("seed", range(8))

@@ -9,6 +9,7 @@ import torch
 
 import synth
 import paged_variable_length_amd as pa
+from bench import TILING as BENCH_TILING
 from paged_variable_length_amd import _abi
 from oracle import attention as oa
 from oracle import fp8 as of
@@ -134,7 +135,7 @@ def test_decode_fp8_full_size_sampled():
     order = np.argsort(w.ctx_lens)
     seqs = sorted(set([int(order[0]), int(order[-1])] +
                       rng.choice(w.num_seqs, 10, replace=False).tolist()))
-    _, out, _ = _decode_case(w, 1024, seqs)
+    _, out, _ = _decode_case(w, BENCH_TILING["decode_mha_fp8"]["dec_split"], seqs)
     assert torch.isfinite(out).all()
 
 
@@ -189,7 +190,8 @@ def test_verify_fp8_full_size_sampled():
     order = np.argsort(w.ctx_lens)
     seqs = sorted(set([int(order[0]), int(order[-1])] +
                       rng.choice(w.num_seqs, 10, replace=False).tolist()))
-    _, out = _verify_case(w, 8192, 4, seqs)
+    tiling = BENCH_TILING["verify_gqa_fp8"]
+    _, out = _verify_case(w, tiling["dec_split"], tiling["verify_rows"], seqs)
     assert torch.isfinite(out).all()
 
 

@@ -13,6 +13,7 @@ import torch
 
 import synth
 import paged_variable_length_amd as pa
+from bench import TILING as BENCH_TILING
 from oracle import attention as oa
 from oracle import cache as oc
 from tests.helpers import check_close, to_np, to_np_raw
@@ -170,8 +171,9 @@ def test_single_key_returns_value_exactly_on_gpu():
 
 @pytest.mark.parametrize("name", ["decode_mha_bf16", "decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64"])
 def test_decode_full_size(name):
-    """Full-size decode workloads in the benchmark's launch configuration; the oracle checks a
-    seeded sample of sequences that always holds the shortest and the longest."""
+    """Full-size decode workloads in the launch configuration bench.py times (its TILING: key
+    splits of 1024 for the MHA batch, 8192 for the GQA batches); the oracle checks a seeded
+    sample of sequences that always holds the shortest and the longest."""
     w = synth.make_workload(name)
     _announce(f"decode full {name} N={w.num_seqs}")
     rng = np.random.default_rng(0)
@@ -181,7 +183,7 @@ def test_decode_full_size(name):
                       rng.choice(w.num_seqs, n_sample, replace=False).tolist()))[:n_sample + 2]
     vals = synth.make_values(w, device=DEV)
     h = host_subset(w, vals, seqs)
-    out, _ = run_gpu(w, vals, "decode", dec_split=512)
+    out, _ = run_gpu(w, vals, "decode", **BENCH_TILING[name])
     ref = oracle_subset(h, 1.0 / math.sqrt(w.head_dim))
     check_close(to_np(out)[h["rows"]], ref, "bf16", name)
     assert torch.isfinite(out).all()
@@ -226,14 +228,15 @@ def test_mixed_decode_and_chunks(bs):
 
 
 def test_prefill_full_size_sampled():
-    """The packed varlen prefill workload at full size; sampled rows of every sequence (first,
-    last, and random rows), all heads, checked one by one against the oracle."""
+    """The packed varlen prefill workload at full size in the launch configuration bench.py
+    times; sampled rows of every sequence (first, last, and random rows), all heads, checked one
+    by one against the oracle."""
     w = synth.make_workload("prefill_varlen_bf16")
     _announce(f"prefill full T={w.num_tokens} lens={w.q_lens.tolist()}")
     vals = synth.make_values(w, device=DEV)
     seqs = list(range(w.num_seqs))
     h = host_subset(w, vals, seqs)
-    out, _ = run_gpu(w, vals, "varlen", pf_q_tile=128, pf_kv_split=0)
+    out, _ = run_gpu(w, vals, "varlen", **BENCH_TILING["prefill_varlen_bf16"])
     rng = np.random.default_rng(1)
     rows = {}
     for i, s in enumerate(seqs):
@@ -246,18 +249,33 @@ def test_prefill_full_size_sampled():
 
 def test_mixed_full_size_sampled():
     """The mixed unified step at full size (200 decode rows + 4 x 512-row chunks over prefixes
-    up to 131072 keys) in one launch; sampled decode sequences and chunk rows vs the oracle."""
+    up to 131072 keys) in one launch, in the launch configuration bench.py times (decode splits
+    of 4096 keys, each 128-row chunk tile over its whole prefix with no key split, so it writes
+    `out` directly). Sampled decode sequences (shortest and longest context included), rows of
+    all four chunks, and in the chunk with the longest prefix the first and last row of every
+    128-row tile, all heads, against the oracle."""
     w = synth.make_workload("mixed_bf16")
-    _announce(f"mixed full T={w.num_tokens} NB={w.num_blocks}")
+    tiling = BENCH_TILING["mixed_bf16"]
+    _announce(f"mixed full T={w.num_tokens} NB={w.num_blocks} {tiling}")
     vals = synth.make_values(w, device=DEV)
     rng = np.random.default_rng(2)
     chunks = sorted(range(200, 204), key=lambda s: int(w.ctx_lens[s]))
-    seqs = sorted(rng.choice(200, 12, replace=False).tolist()) + [chunks[0], chunks[-1]]
+    order = np.argsort(w.ctx_lens[:200])
+    dec = sorted(set(rng.choice(200, 10, replace=False).tolist() +
+                     [int(order[0]), int(order[-1])]))
+    seqs = dec + chunks
     h = host_subset(w, vals, seqs)
-    out, _ = run_gpu(w, vals, "varlen", dec_split=512, pf_q_tile=128, pf_kv_split=8192)
-    rows = {i: [0] for i in range(12)}
-    for i in range(12, 14):
-        rows[i] = [0, 1, 127, 128, 300, 511]
+    out, plan = run_gpu(w, vals, "varlen", **tiling)
+    pf = plan.table.tasks[plan.table.tasks[:, 0] == pa.PA_TASK_PREFILL]
+    assert np.all(pf[:, 7] == -1), "the benched mixed tiling runs prefill tiles unsplit"
+    rows = {i: [0] for i in range(len(dec))}
+    for i, s in enumerate(chunks):
+        ql = int(w.q_lens[s])
+        if s == chunks[-1]:
+            rows[len(dec) + i] = sorted({r for r0 in range(0, ql, 128)
+                                         for r in (r0, min(ql, r0 + 128) - 1)})
+        else:
+            rows[len(dec) + i] = [0, ql // 2 - 1, ql - 1]
     ref = oracle_subset(h, 1.0 / math.sqrt(w.head_dim), sample_rows=rows)
     check_close(to_np(out)[h["rows"]], ref, "bf16", "mixed full")
     assert torch.isfinite(out).all()
@@ -301,7 +319,7 @@ def test_verify_full_size_sampled():
                       rng.choice(w.num_seqs, 30, replace=False).tolist()))
     vals = synth.make_values(w, device=DEV)
     h = host_subset(w, vals, seqs)
-    out, plan = run_gpu(w, vals, "varlen", dec_split=8192, verify_rows=4)
+    out, plan = run_gpu(w, vals, "varlen", **BENCH_TILING["verify_gqa_bf16"])
     assert set(plan.table.tasks[:, 0].tolist()) == {2}
     ref = oracle_subset(h, 1.0 / math.sqrt(w.head_dim))
     check_close(to_np(out)[h["rows"]], ref, "bf16", "verify full")

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import synth
+from bench import TILING as BENCH_TILING
 from paged_variable_length_amd import _abi
 from tests.helpers import aliased_workload
 from tests.test_gpu_parity import _announce, small_case
@@ -54,13 +55,14 @@ def test_shared_in_mixed_launch(seed, G):
 
 
 def test_shared_decode_full_size_sampled():
-    """The 128-request agent batch (8 prompts x 16 requests) in the benchmark's tiling; a seeded
-    sample of requests from every group against the oracle."""
+    """The 128-request agent batch (8 prompts x 16 requests) in the launch configuration
+    bench.py times (its TILING: key splits of 4096, groups from 64 shared keys); a seeded sample
+    of requests from every group against the oracle."""
     w = synth.make_workload("decode_shared_mha_bf16")
     rng = np.random.default_rng(9)
     seqs = sorted(set((16 * np.arange(8) + rng.integers(0, 16, size=8)).tolist() + [0, 127]))
     _announce(f"shared decode full N={w.num_seqs} sampled {seqs}")
-    _, out, _, plan = small_case(w, "decode", seqs=seqs, dec_split=1024, shared_min=64)
+    _, out, _, plan = small_case(w, "decode", seqs=seqs, **BENCH_TILING["decode_shared_mha_bf16"])
     assert _has_shared(plan)
     import torch
     assert torch.isfinite(out).all()
