@@ -270,6 +270,32 @@ int paged_attn_varlen_prefill(const void* q, const void* k_pages, const void* v_
                               int32_t num_combines, int32_t num_partials, void* workspace,
                               size_t workspace_bytes, void* out, void* stream);
 
+/* Bytes of partial rows paged_attn_varlen_prefill_noalloc can hold: 64 MiB, i.e.
+ * pa_workspace_bytes(num_partials, D) <= this (about 129k partial rows at D = 128). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* paged_attn_varlen_prefill without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc). Same arguments, tasks, results and errors as paged_attn_varlen_prefill, minus
+ * workspace and workspace_bytes: the partial rows go to a scratch buffer the library holds in
+ * device memory, PA_NOALLOC_SCRATCH_BYTES per GPU, set up on the first call made with each device
+ * current and kept until the process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other threads) race and must be ordered by the caller. The
+ * scratch keeps the last call's contents; nothing in it needs to start at zero.
+ *   Errors as paged_attn_varlen_prefill, plus PA_ERR_CAPACITY when
+ *   pa_workspace_bytes(num_partials, head_dim) exceeds PA_NOALLOC_SCRATCH_BYTES (then use the
+ *   workspace entry), and PA_ERR_HIP when the scratch's device address cannot be taken. */
+int paged_attn_varlen_prefill_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      float scale, int32_t dtype, const pa_task* tasks_dev,
+                                      int32_t num_tasks, uint32_t task_kinds,
+                                      const pa_combine* combines_dev, int32_t num_combines,
+                                      int32_t num_partials, void* out, void* stream);
+
 /* fp8 KV pages (cann-recipes-infer page, section 5.2: values are scaled before they are
  * stored, and each page keeps its scale factor, multiplied back on reading).
  *   Page format: k_pages, v_pages uint8 [num_blocks, Hkv, block_size, D] holding OCP E4M3FN

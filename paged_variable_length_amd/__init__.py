@@ -11,6 +11,7 @@ falls back to a CPU path: a missing library raises.
     reshape_and_cache        write new K/V rows into their pages (device)
     paged_attn_decode        decode attention, one query token per sequence (device)
     paged_attn_varlen_prefill  packed causal attention, any mix of decode and prefill (device)
+    paged_attn_varlen_prefill_noalloc  the same with partial rows in the library's own scratch
     validate_block_table     debug check of a host block table
     StepPlan                 convenience: a built table copied to the device with its workspace
     build_gemm_table         SmoothGEMM's Linear decomposition: load-sorted tile tasks (host)
@@ -31,7 +32,8 @@ from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F
                    PaGemmTask, PaParams, PaTask, check, lib)
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
-           "paged_attn_decode", "paged_attn_varlen_prefill", "validate_block_table",
+           "paged_attn_decode", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_noalloc",
+           "validate_block_table",
            "reshape_and_cache_fp8", "paged_attn_decode_fp8", "paged_attn_verify_fp8",
            "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32",
            "build_gemm_table", "gemm_workspace_bytes", "smooth_gemm", "GemmTable", "GemmPlan"]
@@ -337,6 +339,26 @@ def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, co
         _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out"), _stream(stream)]
     check(lib().paged_attn_varlen_prefill(*args), "paged_attn_varlen_prefill")
+
+
+def paged_attn_varlen_prefill_noalloc(q, k_pages, v_pages, block_table, cu_seqlens_q,
+                                      context_lens, scale, tasks_dev, task_kinds, combines_dev,
+                                      num_partials, out, stream=None):
+    """paged_attn_varlen_prefill with its partial rows in the library's own device scratch
+    (no workspace argument; nothing is allocated). Calls that overlap on one GPU share that
+    scratch and must be ordered by the caller."""
+    torch = _torch()
+    head = _attn_common(q, k_pages, v_pages, block_table, context_lens, out)
+    T, hq, d = q.shape
+    n = context_lens.shape[0]
+    if cu_seqlens_q.shape[0] != n + 1:
+        raise ValueError("cu_seqlens_q must be [num_seqs + 1]")
+    tbl = _table_args(tasks_dev, task_kinds, combines_dev, num_partials, None)[:-2]
+    args = head + [_dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                   _dev(context_lens, "context_lens", torch.int32), n, T, hq, k_pages.shape[1],
+                   d, k_pages.shape[2], float(scale), _dtype_code(q)] + tbl + \
+        [_dev(out, "out"), _stream(stream)]
+    check(lib().paged_attn_varlen_prefill_noalloc(*args), "paged_attn_varlen_prefill_noalloc")
 
 
 class StepPlan:

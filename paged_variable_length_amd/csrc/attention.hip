@@ -27,6 +27,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -1443,9 +1444,9 @@ int hip_check(const char* what) {
   return pa::clear_error();
 }
 
-int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d,
-                       int32_t bs, int32_t dtype, int32_t num_tasks, int32_t num_combines,
-                       int32_t num_partials, size_t ws_bytes, const void* ws, int32_t max_blocks) {
+int check_attn_shape(const char* who, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d,
+                     int32_t bs, int32_t dtype, int32_t num_tasks, int32_t num_combines,
+                     int32_t num_partials, int32_t max_blocks) {
   if (num_seqs < 0 || num_tasks < 0 || num_combines < 0 || num_partials < 0 || max_blocks < 0)
     return pa::set_error(PA_ERR_SHAPE, "%s: negative size", who);
   if (num_tasks > pa::kMaxWorkgroups || num_combines > pa::kMaxWorkgroups)
@@ -1459,6 +1460,13 @@ int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hk
   if (!pa::block_size_ok(bs))
     return pa::set_error(PA_ERR_BLOCK_SIZE, "%s: block_size %d is not a power of two in [16, 256]", who, bs);
   if (dtype != PA_BF16 && dtype != PA_FP32) return pa::set_error(PA_ERR_DTYPE, "%s: dtype %d", who, dtype);
+  return PA_OK;
+}
+
+// The caller's workspace must hold every partial row whenever the table has partial rows or
+// combine records.
+int check_workspace(const char* who, int32_t num_partials, int32_t num_combines, int32_t d,
+                    size_t ws_bytes, const void* ws) {
   if (num_partials > 0 || num_combines > 0) {
     if (!ws) return pa::set_error(PA_ERR_NULL, "%s: workspace is NULL", who);
     const size_t need = pa_workspace_bytes(num_partials, d);
@@ -1466,6 +1474,15 @@ int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hk
       return pa::set_error(PA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
   }
   return PA_OK;
+}
+
+int check_attn_scalars(const char* who, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t bs, int32_t dtype, int32_t num_tasks, int32_t num_combines,
+                       int32_t num_partials, size_t ws_bytes, const void* ws, int32_t max_blocks) {
+  if (int rc = check_attn_shape(who, num_seqs, hq, hkv, d, bs, dtype, num_tasks, num_combines,
+                                num_partials, max_blocks))
+    return rc;
+  return check_workspace(who, num_partials, num_combines, d, ws_bytes, ws);
 }
 
 // The table's kind mask against the kinds this entry runs: a kind outside `allowed` would be
@@ -1605,30 +1622,41 @@ extern "C" int paged_attn_decode(const void* q, const void* k_pages, const void*
   return hip_check("paged_attn_decode");
 }
 
-extern "C" int paged_attn_varlen_prefill(
-    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* context_lens,
-    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, float scale, int32_t dtype, const pa_task* tasks_dev,
-    int32_t num_tasks, uint32_t task_kinds, const pa_combine* combines_dev,
-    int32_t num_combines, int32_t num_partials, void* workspace, size_t workspace_bytes,
-    void* out, void* stream) {
-  if (int rc = check_attn_scalars("paged_attn_varlen_prefill", num_seqs, num_q_heads,
-                                  num_kv_heads, head_dim, block_size, dtype, num_tasks,
-                                  num_combines, num_partials, workspace_bytes, workspace,
-                                  max_blocks_per_seq))
+namespace {
+
+// The unified launch's checks that need no workspace: shapes, kinds, dtype, token count and the
+// device pointers. PA_OK means the launch may be enqueued (given a workspace).
+int varlen_checks(const char* who, const void* q, const void* k_pages, const void* v_pages,
+                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t dtype, const pa_task* tasks_dev,
+                  int32_t num_tasks, uint32_t task_kinds, const pa_combine* combines_dev,
+                  int32_t num_combines, int32_t num_partials, const void* out) {
+  if (int rc = check_attn_shape(who, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                dtype, num_tasks, num_combines, num_partials, max_blocks_per_seq))
     return rc;
-  if (int rc = check_kinds("paged_attn_varlen_prefill", num_tasks, task_kinds, kAllKinds))
-    return rc;
+  if (int rc = check_kinds(who, num_tasks, task_kinds, kAllKinds)) return rc;
   if (dtype != PA_BF16)
-    return pa::set_error(PA_ERR_DTYPE, "paged_attn_varlen_prefill: the MFMA path needs PA_BF16");
+    return pa::set_error(PA_ERR_DTYPE, "%s: the MFMA path needs PA_BF16", who);
   if (num_tokens < num_seqs)
-    return pa::set_error(PA_ERR_SHAPE, "paged_attn_varlen_prefill: %d tokens for %d sequences",
-                         num_tokens, num_seqs);
-  if (num_tasks == 0) return pa::clear_error();
+    return pa::set_error(PA_ERR_SHAPE, "%s: %d tokens for %d sequences", who, num_tokens,
+                         num_seqs);
+  if (num_tasks == 0) return PA_OK;
   if (!q || !k_pages || !v_pages || !block_table || !cu_seqlens_q || !context_lens || !out ||
       !tasks_dev || (num_combines > 0 && !combines_dev))
-    return pa::set_error(PA_ERR_NULL, "paged_attn_varlen_prefill: NULL pointer");
+    return pa::set_error(PA_ERR_NULL, "%s: NULL pointer", who);
+  return PA_OK;
+}
+
+// The unified launch and its combine, on `stream`, with partial rows in `workspace`.
+int varlen_enqueue(const char* who, const void* q, const void* k_pages, const void* v_pages,
+                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                   const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, float scale, const pa_task* tasks_dev, int32_t num_tasks,
+                   const pa_combine* combines_dev, int32_t num_combines, int32_t num_partials,
+                   void* workspace, void* out, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq,
                                cu_seqlens_q, context_lens, num_q_heads, num_kv_heads, head_dim,
@@ -1641,7 +1669,103 @@ extern "C" int paged_attn_varlen_prefill(
     hipLaunchKernelGGL(meta_attn_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
   }
-  return hip_check("paged_attn_varlen_prefill");
+  return hip_check(who);
+}
+
+}  // namespace
+
+extern "C" int paged_attn_varlen_prefill(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float scale, int32_t dtype, const pa_task* tasks_dev,
+    int32_t num_tasks, uint32_t task_kinds, const pa_combine* combines_dev,
+    int32_t num_combines, int32_t num_partials, void* workspace, size_t workspace_bytes,
+    void* out, void* stream) {
+  const char* who = "paged_attn_varlen_prefill";
+  if (int rc = varlen_checks(who, q, k_pages, v_pages, block_table, max_blocks_per_seq,
+                             cu_seqlens_q, context_lens, num_seqs, num_tokens, num_q_heads,
+                             num_kv_heads, head_dim, block_size, dtype, tasks_dev, num_tasks,
+                             task_kinds, combines_dev, num_combines, num_partials, out))
+    return rc;
+  if (int rc = check_workspace(who, num_partials, num_combines, head_dim, workspace_bytes,
+                               workspace))
+    return rc;
+  if (num_tasks == 0) return pa::clear_error();
+  return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
+                        context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                        tasks_dev, num_tasks, combines_dev, num_combines, num_partials,
+                        workspace, out, stream);
+}
+
+// Partial rows of paged_attn_varlen_prefill_noalloc: device memory the library holds itself.
+// Each GPU the library runs on gets its own copy when the code object is loaded there, kept until
+// the process ends. In host code `scratch` names a host-side stand-in, not device memory: only
+// the per-device addresses from hipGetSymbolAddress are ever passed to kernels.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call made with
+// that device current and kept for later calls.
+int scratch_of_current_device(const char* who, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return pa::set_error(PA_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return pa::set_error(PA_ERR_HIP, "%s: device %d beyond the %d this library tracks", who, dev,
+                         kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return pa::set_error(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                           hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int paged_attn_varlen_prefill_noalloc(
+    const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float scale, int32_t dtype, const pa_task* tasks_dev,
+    int32_t num_tasks, uint32_t task_kinds, const pa_combine* combines_dev,
+    int32_t num_combines, int32_t num_partials, void* out, void* stream) {
+  const char* who = "paged_attn_varlen_prefill_noalloc";
+  if (int rc = varlen_checks(who, q, k_pages, v_pages, block_table, max_blocks_per_seq,
+                             cu_seqlens_q, context_lens, num_seqs, num_tokens, num_q_heads,
+                             num_kv_heads, head_dim, block_size, dtype, tasks_dev, num_tasks,
+                             task_kinds, combines_dev, num_combines, num_partials, out))
+    return rc;
+  const bool partials = num_partials > 0 || num_combines > 0;
+  if (partials) {
+    const size_t need = pa_workspace_bytes(num_partials, head_dim);
+    if (need > PA_NOALLOC_SCRATCH_BYTES)
+      return pa::set_error(PA_ERR_CAPACITY,
+                           "%s: %d partial rows need %zu bytes; this entry holds %zu (use "
+                           "paged_attn_varlen_prefill with a workspace)",
+                           who, num_partials, need, static_cast<size_t>(PA_NOALLOC_SCRATCH_BYTES));
+  }
+  if (num_tasks == 0) return pa::clear_error();
+  // every partial row the combine reads is written by a task of the same launch before it, so
+  // nothing in the scratch has to start at zero
+  void* ws = nullptr;
+  if (partials)
+    if (int rc = scratch_of_current_device(who, &ws)) return rc;
+  return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
+                        context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                        tasks_dev, num_tasks, combines_dev, num_combines, num_partials, ws, out,
+                        stream);
 }
 
 extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages,

@@ -311,6 +311,34 @@ def test_attention_entries_refuse_task_kinds_they_do_not_run():
     assert verify_fp8(t.kinds) == _abi.PA_ERR_NULL
 
 
+def test_noalloc_entry_checks_need_no_gpu():
+    """The allocation-free unified entry refuses, before any HIP call, a table whose partial
+    rows exceed its fixed scratch, and shares the unified entry's other checks."""
+    L = _abi.lib()
+    p = ctypes.c_void_p(256)
+    fn = L.paged_attn_varlen_prefill_noalloc
+    # 200000 partial rows at D = 128 need ~104 MB > 64 MiB of scratch
+    big = 200000
+    assert pa.workspace_bytes(big, 128) > _abi.NOALLOC_SCRATCH_BYTES
+    rc = fn(p, p, p, p, 1, p, p, 1, 2, 8, 2, 128, 16, 0.1, 0, p, 1, 1, p, 1, big, p, None)
+    assert rc == _abi.PA_ERR_CAPACITY
+    assert b"paged_attn_varlen_prefill with a workspace" in L.pa_last_error()
+    # at the limit the size check passes and the NULL context_lens is what stops the call
+    fit = (_abi.NOALLOC_SCRATCH_BYTES - 256) // (4 * 130)
+    assert pa.workspace_bytes(fit, 128) <= _abi.NOALLOC_SCRATCH_BYTES
+    rc = fn(p, p, p, p, 1, p, None, 1, 2, 8, 2, 128, 16, 0.1, 0, p, 1, 1, p, 1, fit, p, None)
+    assert rc == _abi.PA_ERR_NULL
+    # the unified entry's own checks: dtype, kinds, token count; an empty table is a no-op
+    assert fn(p, p, p, p, 1, p, p, 1, 2, 8, 2, 128, 16, 0.1, 1, p, 1, 1, p, 1, 8, p,
+              None) == _abi.PA_ERR_DTYPE
+    assert fn(p, p, p, p, 1, p, p, 1, 2, 8, 2, 128, 16, 0.1, 0, p, 1, 0, p, 1, 8, p,
+              None) == _abi.PA_ERR_INPUT
+    assert fn(p, p, p, p, 1, p, p, 3, 2, 8, 2, 128, 16, 0.1, 0, p, 1, 1, p, 1, 8, p,
+              None) == _abi.PA_ERR_SHAPE
+    assert fn(None, None, None, None, 1, None, None, 1, 1, 8, 2, 128, 16, 0.1, 0, None, 0, 0,
+              None, 0, 0, None, None) == _abi.PA_OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
