@@ -13,6 +13,10 @@ out, the block-table entries read) over the measured step time. Secondary worklo
 JSON line: GQA decode at block sizes 16 and 64, the packed varlen causal prefill (TFLOP/s) and
 the mixed unified step (both). `roofline` covers the attention launch of the headline workload,
 timed with HIP events on the launch stream, with L2/MALL evicted (a 1 GiB read) between launches.
+The fp64 oracle is timed on this host's cores on a bounded sample: whole sequences of the
+headline batch (`cpu_baseline`, GB/s) and sampled query rows of the prefill and mixed workloads
+(their `cpu_baseline` entries, GFLOP/s). `context_sweep` runs the headline batch's shape at one
+context per run (256 .. 16384 keys) and fits launch time against context length.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--only] [--no-cpu-baseline]
 """
@@ -77,6 +81,8 @@ GEMM_TILING = {
     "gemm_linear_2048x512x2048": dict(tile=128, k_split=0, tail_split=True),
 }
 GEMM_WORKERS = 256      # resident workgroups: one per CU for both tiles
+# workloads whose oracle baseline is timed on sampled query rows (GFLOP/s)
+ROW_SAMPLED_BASELINE = ("prefill_varlen_bf16", "mixed_bf16")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_variable_length_amd", "csrc", "attention.hip")
 
 
@@ -157,19 +163,20 @@ def algorithmic_work(w, fp8_pages=False):
 class Runner:
     """Everything one workload's step needs, resident on the GPU."""
 
-    def __init__(self, name, seed=None):
+    def __init__(self, name, seed=None, workload=None, tiling=None):
         import torch
         import synth
         import paged_variable_length_amd as pa
         self.torch, self.pa = torch, pa
         self.name = name
-        self.w = w = synth.make_workload(name.split(":")[0], seed)   # "name:variant" tilings
+        # "name:variant" tilings; a caller-built workload (the context sweep) brings its tiling
+        self.w = w = workload if workload is not None else synth.make_workload(name.split(":")[0], seed)
         self.vals = synth.make_values(w, device="cuda", nan_sentinels=True)
         self.fp8 = name.endswith("_fp8")
         if self.fp8:                     # fp8 pages with page scales replace the bf16 pool
             del self.vals["k_pages"], self.vals["v_pages"]
             self.vals.update(synth.make_fp8_pages(w, device="cuda"))
-        self.tiling = dict(TILING[name], num_workers=256 * 2)
+        self.tiling = dict(tiling if tiling is not None else TILING[name], num_workers=256 * 2)
         self.cu_host = pa.pack_seqlens(w.q_lens)
         self.ctx_host = w.ctx_lens.astype(np.int32)
         self.params = pa.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
@@ -330,6 +337,33 @@ class Runner:
         return bool(self.torch.isfinite(self.out).all())
 
 
+def host_cpu():
+    """BLAS threads the oracle's NumPy uses, the cores this process may run on, and the host
+    CPU as /proc/cpuinfo names it (model name plus family / model / stepping numbers)."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    fields = {}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+            if not line.strip() and fields:
+                break
+    except OSError:
+        pass
+    model = fields.get("model name", "unknown")
+    if "cpu family" in fields:
+        model += (f" (family {fields['cpu family']}, model {fields.get('model', '?')}, "
+                  f"stepping {fields.get('stepping', '?')})")
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return threads, model, affinity
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded seeded sample of the same workload's
     sequences (cache scatter + attention), timed on this host's cores."""
@@ -345,20 +379,7 @@ def cpu_baseline(name, budget_s=12.0):
     e_kv = 2 * w.num_kv_heads * w.head_dim * esize
     cu = oa.pack_lengths(w.q_lens)
     done_bytes, done_seqs, spent = 0, 0, 0.0
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    model = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    threads, model, affinity = host_cpu()
     for s in order:
         s = int(s)
         nblk = oa.blocks_needed(int(w.ctx_lens[s]), w.block_size)
@@ -386,6 +407,112 @@ def cpu_baseline(name, budget_s=12.0):
             "kind": "oracle", "cpu_model": model, "cores_available": affinity,
             "sample": f"{done_seqs} of {w.num_seqs} sequences of {name} (seeded order), "
                       f"fp64 NumPy cache scatter + attention, {spent:.1f} s"}
+
+
+def cpu_baseline_rows(name, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded seeded sample of a prefill or mixed
+    workload's query rows, timed on this host's cores. The sequence with the longest context
+    comes first, then the others in a seeded order; in the first pass each contributes its first
+    and last row and one seeded row (a decode sequence its one row), and while the time budget
+    lasts further passes add seeded rows of the multi-row sequences. Every sampled row runs for
+    all query heads through the oracle's plain definition (gather through the block table,
+    full-row softmax per row and head). Reported in GFLOP/s of the sampled rows' flops (4 * D
+    per visible key per head); for sampled decode rows also their K/V bytes per second."""
+    import torch
+    import synth
+    from oracle import attention as oa
+    w = synth.make_workload(name.split(":")[0])
+    vals = synth.make_values(w, device="cuda", nan_sentinels=False)
+    rng = np.random.default_rng(0)
+    longest = int(np.argmax(w.ctx_lens))
+    order = [longest] + [int(x) for x in rng.permutation(w.num_seqs) if int(x) != longest]
+    cu = oa.pack_lengths(w.q_lens)
+    e_kv = 2 * w.num_kv_heads * w.head_dim * 2
+    scale = 1.0 / math.sqrt(w.head_dim)
+    flops, dec_bytes, dec_time, spent, nrows = 0, 0, 0.0, 0.0, 0
+    seen, host = set(), {}
+    threads, model, affinity = host_cpu()
+
+    def host_copy(s):
+        if s not in host:
+            nblk = oa.blocks_needed(int(w.ctx_lens[s]), w.block_size)
+            ids = torch.from_numpy(w.block_table[s, :nblk].astype(np.int64)).cuda()
+            f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+            host[s] = (f64(vals["k_pages"].index_select(0, ids)),
+                       f64(vals["v_pages"].index_select(0, ids)),
+                       f64(vals["q"][int(cu[s]):int(cu[s + 1])]), np.arange(nblk)[None, :])
+        return host[s]
+
+    for rnd in range(64):
+        for s in order:
+            ql, ctx = int(w.q_lens[s]), int(w.ctx_lens[s])
+            if rnd > 0 and ql == 1:
+                continue
+            rows = sorted({0, ql - 1, int(rng.integers(0, ql))}) if rnd == 0 else \
+                sorted({int(x) for x in rng.integers(0, ql, size=4)})
+            kp, vp, q, table = host_copy(s)
+            t0 = time.perf_counter()
+            oa.paged_attention(q, kp, vp, table, w.q_lens[s:s + 1], w.ctx_lens[s:s + 1], scale,
+                               rows={0: rows})
+            dt = time.perf_counter() - t0
+            spent += dt
+            flops += sum(ctx - ql + i + 1 for i in rows) * w.num_q_heads * 4 * w.head_dim
+            if ql == 1:
+                dec_bytes += ctx * e_kv
+                dec_time += dt
+            seen.add(s)
+            nrows += len(rows)
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    del vals, host
+    torch.cuda.empty_cache()
+    out = {"value": round(flops / spent / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
+           "kind": "oracle", "cpu_model": model, "cores_available": affinity,
+           "sample": f"{nrows} query rows x {w.num_q_heads} heads from {len(seen)} of "
+                     f"{w.num_seqs} sequences of {name} (longest context first, then seeded), "
+                     f"fp64 NumPy gather + full-row softmax per row, {spent:.1f} s, "
+                     f"{flops:.3e} flop"}
+    if dec_time > 0:
+        out["decode_rows_gbs"] = round(dec_bytes / dec_time / 1e9, 4)
+    return out
+
+
+# Context-length sweep of the headline decode batch's shape (cann-recipes-infer page, section
+# 4.4, third check: the paged-attention kernel's time grows linearly with the sequence length
+# while its read bandwidth stays steady): 64 sequences, all with the same context, MHA 32 heads,
+# D 128, 16-token blocks, the headline tiling.
+SWEEP_CTX = (256, 512, 1024, 2048, 4096, 8192, 16384)
+
+
+def ctx_sweep(launches, flush):
+    import synth
+    points = []
+    for ctx in SWEEP_CTX:
+        w = synth.custom_workload([1] * 64, [ctx] * 64, 32, 32, 128, 16, seed=8,
+                                  name=f"decode_mha_bf16_ctx{ctx}")
+        r = Runner(w.name, workload=w, tiling=TILING[HEADLINE])
+        avg, mn = r.launch_times(launches, flush)
+        b = r.work["bytes"]
+        points.append({"context": ctx, "launch_ms_avg": round(avg, 4),
+                       "launch_ms_median": round(r.last_launch_median, 4),
+                       "bytes": b, "gbs": round(b / (avg * 1e-3) / 1e9, 1)})
+        del r
+        import torch
+        torch.cuda.empty_cache()
+    x = np.array([p["context"] for p in points], dtype=np.float64)
+    y = np.array([p["launch_ms_avg"] for p in points], dtype=np.float64)
+    slope, icept = np.polyfit(x, y, 1)
+    pred = slope * x + icept
+    r2 = 1.0 - float(((y - pred) ** 2).sum() / ((y - y.mean()) ** 2).sum())
+    gbs = [p["gbs"] for p in points]
+    return {"batch": "64 decode sequences, one context each run, Hq=Hkv=32, D=128, bs=16",
+            "points": points,
+            "linear_fit_ms": {"per_1k_keys": round(slope * 1e3, 5), "intercept": round(icept, 5),
+                              "r2": round(r2, 5)},
+            "gbs_from_2048": {"min": min(g for p, g in zip(points, gbs) if p["context"] >= 2048),
+                              "max": max(g for p, g in zip(points, gbs) if p["context"] >= 2048)}}
 
 
 def run_gemm(name, steps, warmup, flush):
@@ -563,11 +690,23 @@ def main():
             res["roofline_frac"] = round(max(wk["bytes"] / (HBM_PEAK_GBS * 1e9),
                                              wk["flops_prefill"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / t_launch, 4)
+            if name in ROW_SAMPLED_BASELINE and not args.no_cpu_baseline:
+                cb = cpu_baseline_rows(name)
+                res["cpu_baseline"] = cb
+                res["gpu_over_cpu_baseline"] = round(res["attn_tflops_prefill"] * 1e3 / cb["value"], 1)
+                print(f"[bench] {name}: oracle {cb['value']} GFLOP/s on {cb['cores']} threads "
+                      f"({cb['sample']})", file=sys.stderr, flush=True)
             secondary[name] = res
             print(f"[bench] {name}: {res['ms_per_step']} ms/step, launch "
                   f"{res['attn_launch_ms_avg']} ms, {res['attn_gbs']} GB/s, "
                   f"{res['attn_tflops_prefill']} TFLOP/s", file=sys.stderr, flush=True)
 
+    sweep = None
+    if not args.only:
+        sweep = ctx_sweep(max(args.steps, 10), flush)
+        fit = sweep["linear_fit_ms"]
+        print(f"[bench] context sweep: {fit['per_1k_keys']} ms per 1k keys, r2 {fit['r2']}, "
+              f"GB/s from 2k keys {sweep['gbs_from_2048']}", file=sys.stderr, flush=True)
     wk = head["work"]
     step_s = head["ms_per_step"] * 1e-3
     value = wk["bytes"] / step_s / 1e9
@@ -612,6 +751,7 @@ def main():
                                                  "attn_launch_ms_median",
                                                  "reshape_ms_avg", "reshape_gbs")},
         "secondary": secondary,
+        "context_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 
