@@ -230,7 +230,7 @@ class Runner:
         pa, v = self.pa, self.vals
         if self.fp8:
             pa.reshape_and_cache_fp8(v["k_new"], v["v_new"], v["k_codes"], v["v_codes"],
-                                     v["k_scales"], v["v_scales"], self.bt, self.cu, self.ctx)
+                                     v["scales"], self.bt, self.cu, self.ctx)
         else:
             pa.reshape_and_cache(v["k_new"], v["v_new"], v["k_pages"], v["v_pages"], self.bt,
                                  self.cu, self.ctx)
@@ -248,12 +248,12 @@ class Runner:
         if ev_pair is not None:
             ev_pair[0].record()
         if self.fp8 and self.decode_only:
-            pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
-                                     v["v_scales"], self.bt, self.ctx, self.scale, tasks,
+            pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["scales"],
+                                     self.bt, self.ctx, self.scale, tasks,
                                      self.kinds, combines, nparts, self.ws, self.out)
         elif self.fp8:
-            pa.paged_attn_verify_fp8(v["q"], v["k_codes"], v["v_codes"], v["k_scales"],
-                                     v["v_scales"], self.bt, self.cu, self.ctx, self.scale,
+            pa.paged_attn_verify_fp8(v["q"], v["k_codes"], v["v_codes"], v["scales"],
+                                     self.bt, self.cu, self.ctx, self.scale,
                                      tasks, self.kinds, combines, nparts, self.ws, self.out)
         elif self.decode_only:
             pa.paged_attn_decode(v["q"], v["k_pages"], v["v_pages"], self.bt, self.ctx, self.scale,

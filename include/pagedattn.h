@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 8
+#define PA_ABI_VERSION 9
 
 enum pa_status {
   PA_OK = 0,
@@ -299,8 +299,9 @@ int paged_attn_varlen_prefill_noalloc(const void* q, const void* k_pages, const 
 /* fp8 KV pages (cann-recipes-infer page, section 5.2: values are scaled before they are
  * stored, and each page keeps its scale factor, multiplied back on reading).
  *   Page format: k_pages, v_pages uint8 [num_blocks, Hkv, block_size, D] holding OCP E4M3FN
- *   codes; k_scales, v_scales float [num_blocks, Hkv], one scale per (block, kv head) page, always
- *   a power of two; a cached value is code * scale.
+ *   codes; scales float [num_blocks, Hkv, 2]: for each (block, kv head) the scale of its K page,
+ *   then that of its V page (side by side, so attention fetches both in one 8-byte read), always
+ *   powers of two; a cached value is code * scale.
  *
  * Cache write into fp8 pages: same rows and slots as reshape_and_cache (k_new, v_new bf16
  * [num_tokens, Hkv, D]). Every page this step writes into is rescaled: its valid rows (those
@@ -311,7 +312,7 @@ int paged_attn_varlen_prefill_noalloc(const void* q, const void* k_pages, const 
  * page that holds no row before this step is not read.
  *   Errors: as reshape_and_cache (no dtype argument: the inputs are bf16). */
 int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
-                          float* k_scales, float* v_scales, const int32_t* block_table,
+                          float* scales, const int32_t* block_table,
                           int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
                           int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
@@ -322,8 +323,8 @@ int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages, v
  * runs PA_TASK_DECODE and PA_TASK_SHARED tasks: task_kinds may hold those two only (a table
  * built with verify_rows = 0 from one-row sequences). Errors as paged_attn_decode. */
 int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
-                          const float* k_scales, const float* v_scales,
-                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const float* scales, const int32_t* block_table,
+                          int32_t max_blocks_per_seq,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           float scale, const pa_task* tasks_dev, int32_t num_tasks,
@@ -339,12 +340,12 @@ int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_page
  * (built with verify_rows > 0): each verify row sees the keys up to and including its own
  * position. task_kinds may hold PA_TASK_DECODE and PA_TASK_VERIFY only (prefill and
  * shared-prefix tasks are refused with PA_ERR_INPUT).
- *   Device pointers: q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
- *   context_lens, tasks_dev, combines_dev, workspace, out.
+ *   Device pointers: q, k_pages, v_pages, scales, block_table, cu_seqlens_q, context_lens,
+ *   tasks_dev, combines_dev, workspace, out.
  *   Errors as paged_attn_decode_fp8, plus PA_ERR_SHAPE for num_tokens < num_seqs. */
 int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_pages,
-                          const float* k_scales, const float* v_scales,
-                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const float* scales, const int32_t* block_table,
+                          int32_t max_blocks_per_seq,
                           const int32_t* cu_seqlens_q, const int32_t* context_lens,
                           int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -192,23 +192,24 @@ def reshape_and_cache(k_new, v_new, k_pages, v_pages, block_table, cu_seqlens_q,
     check(lib().reshape_and_cache(*args), "reshape_and_cache")
 
 
-def reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, k_scales, v_scales, block_table,
+def reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, scales, block_table,
                           cu_seqlens_q, context_lens, stream=None):
     """Write packed bf16 rows [T, Hkv, D] into fp8 pages (uint8 [NB, Hkv, bs, D]) with float32
-    page scales [NB, Hkv], rescaling every page the step writes into (library kernel)."""
+    page scales [NB, Hkv, 2] (K then V per page), rescaling every page the step writes into
+    (library kernel)."""
     torch = _torch()
     T, hkv, d = k_new.shape
     nb, hkv2, bs, d2 = k_pages.shape
     if (hkv, d) != (hkv2, d2) or v_new.shape != k_new.shape or v_pages.shape != k_pages.shape:
         raise ValueError("k/v shapes disagree")
-    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
-        raise ValueError("page scales must be [num_blocks, Hkv]")
+    if tuple(scales.shape) != (nb, hkv, 2):
+        raise ValueError("page scales must be [num_blocks, Hkv, 2]")
     n = context_lens.shape[0]
     if block_table.dim() != 2 or block_table.shape[0] != n or cu_seqlens_q.shape[0] != n + 1:
         raise ValueError("block_table / cu_seqlens_q / context_lens sizes disagree")
     args = [_dev(k_new, "k_new", torch.bfloat16, 3), _dev(v_new, "v_new", torch.bfloat16, 3),
             _dev(k_pages, "k_pages", torch.uint8, 4), _dev(v_pages, "v_pages", torch.uint8, 4),
-            _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32),
+            _dev(scales, "scales", torch.float32),
             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
             _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
             _dev(context_lens, "context_lens", torch.int32), n, T, nb, hkv, d, bs,
@@ -265,25 +266,24 @@ def paged_attn_decode(q, k_pages, v_pages, block_table, context_lens, scale, tas
     check(lib().paged_attn_decode(*args), "paged_attn_decode")
 
 
-def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, context_lens,
+def paged_attn_decode_fp8(q, k_pages, v_pages, scales, block_table, context_lens,
                           scale, tasks_dev, task_kinds, combines_dev, num_partials, workspace,
                           out, stream=None):
     """Decode attention over fp8 pages with page scales (library kernels). q/out bf16
-    [N, Hq, D]; pages uint8 [NB, Hkv, bs, D]; scales float32 [NB, Hkv]."""
+    [N, Hq, D]; pages uint8 [NB, Hkv, bs, D]; scales float32 [NB, Hkv, 2]."""
     torch = _torch()
     if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
         raise ValueError("k_pages and v_pages must both be [NB, Hkv, bs, D]")
     if q.dim() != 3 or out.shape != q.shape or q.shape[2] != k_pages.shape[3]:
         raise ValueError("q and out must both be [N, Hq, D] with the pages' head_dim")
     nb, hkv = k_pages.shape[:2]
-    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
-        raise ValueError("page scales must be [num_blocks, Hkv]")
+    if tuple(scales.shape) != (nb, hkv, 2):
+        raise ValueError("page scales must be [num_blocks, Hkv, 2]")
     n, hq, d = q.shape
     if context_lens.shape[0] != n or block_table.dim() != 2 or block_table.shape[0] != n:
         raise ValueError("decode takes one query row per sequence")
     args = [_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
-            _dev(v_pages, "v_pages", torch.uint8), _dev(k_scales, "k_scales", torch.float32),
-            _dev(v_scales, "v_scales", torch.float32),
+            _dev(v_pages, "v_pages", torch.uint8), _dev(scales, "scales", torch.float32),
             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
             _dev(context_lens, "context_lens", torch.int32), n, hq, hkv, d, k_pages.shape[2],
             float(scale)] + \
@@ -292,7 +292,7 @@ def paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, 
     check(lib().paged_attn_decode_fp8(*args), "paged_attn_decode_fp8")
 
 
-def paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, cu_seqlens_q,
+def paged_attn_verify_fp8(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
                           context_lens, scale, tasks_dev, task_kinds, combines_dev, num_partials,
                           workspace, out, stream=None):
     """Decode rows and speculative drafts over fp8 pages with page scales (library kernels).
@@ -304,15 +304,14 @@ def paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, block_table, 
     if q.dim() != 3 or out.shape != q.shape or q.shape[2] != k_pages.shape[3]:
         raise ValueError("q and out must both be [T, Hq, D] with the pages' head_dim")
     nb, hkv = k_pages.shape[:2]
-    if k_scales.shape != (nb, hkv) or v_scales.shape != (nb, hkv):
-        raise ValueError("page scales must be [num_blocks, Hkv]")
+    if tuple(scales.shape) != (nb, hkv, 2):
+        raise ValueError("page scales must be [num_blocks, Hkv, 2]")
     t, hq, d = q.shape
     n = context_lens.shape[0]
     if cu_seqlens_q.shape[0] != n + 1 or block_table.dim() != 2 or block_table.shape[0] != n:
         raise ValueError("block_table / cu_seqlens_q / context_lens sizes disagree")
     args = [_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
-            _dev(v_pages, "v_pages", torch.uint8), _dev(k_scales, "k_scales", torch.float32),
-            _dev(v_scales, "v_scales", torch.float32),
+            _dev(v_pages, "v_pages", torch.uint8), _dev(scales, "scales", torch.float32),
             _dev(block_table, "block_table", torch.int32), block_table.shape[1],
             _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
             _dev(context_lens, "context_lens", torch.int32), n, t, hq, hkv, d, k_pages.shape[2],
@@ -406,22 +405,22 @@ class StepPlan:
                           self.table.kinds, self.combines, self.num_partials, self.workspace, out,
                           stream)
 
-    def write_cache_fp8(self, k_new, v_new, k_pages, v_pages, k_scales, v_scales, stream=None):
-        reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, k_scales, v_scales,
+    def write_cache_fp8(self, k_new, v_new, k_pages, v_pages, scales, stream=None):
+        reshape_and_cache_fp8(k_new, v_new, k_pages, v_pages, scales,
                               self.block_table, self.cu, self.ctx, stream)
 
-    def decode_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
+    def decode_fp8(self, q, k_pages, v_pages, scales, scale, out, stream=None):
         self._check_decode_table("decode_fp8")
-        paged_attn_decode_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table,
+        paged_attn_decode_fp8(q, k_pages, v_pages, scales, self.block_table,
                               self.ctx, scale, self.tasks, self.table.kinds, self.combines,
                               self.num_partials, self.workspace, out, stream)
 
-    def verify_fp8(self, q, k_pages, v_pages, k_scales, v_scales, scale, out, stream=None):
+    def verify_fp8(self, q, k_pages, v_pages, scales, scale, out, stream=None):
         kinds = set(np.unique(self.table.tasks[:, 0]).tolist()) if len(self.table.tasks) else set()
         if not kinds <= {PA_TASK_DECODE, PA_TASK_VERIFY}:
             raise ValueError("verify_fp8 runs decode and verify tasks only: build the table with "
                              "verify_rows covering every draft and shared_min 0")
-        paged_attn_verify_fp8(q, k_pages, v_pages, k_scales, v_scales, self.block_table, self.cu,
+        paged_attn_verify_fp8(q, k_pages, v_pages, scales, self.block_table, self.cu,
                               self.ctx, scale, self.tasks, self.table.kinds, self.combines,
                               self.num_partials, self.workspace, out, stream)
 

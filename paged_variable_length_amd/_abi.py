@@ -27,7 +27,7 @@ PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
 ALL_KINDS = 0xF          # PA_KIND_BIT of every task kind
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -130,14 +130,14 @@ def lib() -> ctypes.CDLL:
                                                     i32, i32, ctypes.c_float, i32, p, i32, u32, p,
                                                     i32, i32, p, p]
     L.reshape_and_cache_fp8.restype = ctypes.c_int
-    L.reshape_and_cache_fp8.argtypes = [p, p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+    L.reshape_and_cache_fp8.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                         i32, p]
     L.paged_attn_decode_fp8.restype = ctypes.c_int
-    L.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
+    L.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32,
                                         ctypes.c_float, p, i32, u32, p, i32, i32, p,
                                         ctypes.c_size_t, p, p]
     L.paged_attn_verify_fp8.restype = ctypes.c_int
-    L.paged_attn_verify_fp8.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+    L.paged_attn_verify_fp8.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                         i32, ctypes.c_float, p, i32, u32, p, i32, i32, p,
                                         ctypes.c_size_t, p, p]
     L.pa_validate_block_table.restype = ctypes.c_int

@@ -56,8 +56,7 @@ struct AttnArgs {
   float* ws_acc;                // [num_partials, D]
   float* ws_ml;                 // [num_partials, 2] (running max in log2 units, sum)
   void* out;
-  const float* k_scales;        // fp8 pages: [num_blocks, Hkv] scale per (block, kv head) page
-  const float* v_scales;
+  const float* scales;          // fp8 pages: [num_blocks, Hkv, 2] (K, V) scales per page
   int32_t max_blocks;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -421,9 +420,11 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         r.v[4 * tt + e] = *reinterpret_cast<const VRaw*>(vbase + off + (4 * g4 + e) * D + VEC * i16);
+      // the K and V scales of a page sit side by side: one 8-byte read
       const size_t page = static_cast<size_t>(blk[tt]) * a.num_kv_heads + kvh;
-      r.ksc[tt] = a.k_scales[page];
-      r.vsc[tt] = a.v_scales[page];
+      const f32x2 sc = *reinterpret_cast<const f32x2*>(a.scales + 2 * page);
+      r.ksc[tt] = sc[0];
+      r.vsc[tt] = sc[1];
     }
   };
 
@@ -1342,7 +1343,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
     const __bf16* k_new, const __bf16* v_new, uint8_t* k_pages, uint8_t* v_pages,
-    float* k_scales, float* v_scales, const int32_t* block_table, int32_t max_blocks,
+    float* scales, const int32_t* block_table, int32_t max_blocks,
     const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_kv_heads, int32_t block_size, int32_t bs_shift) {
   const int unit = blockIdx.y * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1369,7 +1370,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
   const int g = unit - which * num_kv_heads;
   uint8_t* codes = (which ? v_pages : k_pages) +
                    (static_cast<size_t>(blk) * num_kv_heads + g) * block_size * D;
-  float* scale_p = (which ? v_scales : k_scales) + static_cast<size_t>(blk) * num_kv_heads + g;
+  float* scale_p = scales + 2 * (static_cast<size_t>(blk) * num_kv_heads + g) + which;
   const __bf16* src = (which ? v_new : k_new) + g * D;
   const int64_t tok_p = static_cast<int64_t>(cu_seqlens[s]) - P;  // packed token of position 0
   const float old_scale = n_old > 0 ? *scale_p : 1.f;
@@ -1518,8 +1519,7 @@ AttnArgs make_args(const void* q, const void* kp, const void* vp, const int32_t*
   size_t acc_bytes = (static_cast<size_t>(num_partials) * d * sizeof(float) + 255) & ~size_t(255);
   a.ws_ml = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + acc_bytes) : nullptr;
   a.out = out;
-  a.k_scales = nullptr;
-  a.v_scales = nullptr;
+  a.scales = nullptr;
   a.max_blocks = max_blocks;
   a.num_q_heads = hq;
   a.num_kv_heads = hkv;
@@ -1769,7 +1769,7 @@ extern "C" int paged_attn_varlen_prefill_noalloc(
 }
 
 extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages,
-                                     void* v_pages, float* k_scales, float* v_scales,
+                                     void* v_pages, float* scales,
                                      const int32_t* block_table, int32_t max_blocks_per_seq,
                                      const int32_t* cu_seqlens_q, const int32_t* context_lens,
                                      int32_t num_seqs, int32_t num_tokens, int32_t num_blocks,
@@ -1787,8 +1787,8 @@ extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void*
   if (!pa::block_size_ok(block_size))
     return pa::set_error(PA_ERR_BLOCK_SIZE, "reshape_and_cache_fp8: block_size %d", block_size);
   if (num_tokens == 0) return pa::clear_error();
-  if (!k_new || !v_new || !k_pages || !v_pages || !k_scales || !v_scales || !block_table ||
-      !cu_seqlens_q || !context_lens)
+  if (!k_new || !v_new || !k_pages || !v_pages || !scales || !block_table || !cu_seqlens_q ||
+      !context_lens)
     return pa::set_error(PA_ERR_NULL, "reshape_and_cache_fp8: NULL pointer");
   if (num_seqs < 1)
     return pa::set_error(PA_ERR_SHAPE, "reshape_and_cache_fp8: tokens without sequences");
@@ -1798,8 +1798,8 @@ extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void*
 #define PA_RC8_LAUNCH(DD)                                                                      \
   hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DD>, dim3(num_tokens, units), dim3(kThreads), 0, st, \
                      static_cast<const __bf16*>(k_new), static_cast<const __bf16*>(v_new),      \
-                     static_cast<uint8_t*>(k_pages), static_cast<uint8_t*>(v_pages), k_scales,  \
-                     v_scales, block_table, max_blocks_per_seq, cu_seqlens_q, context_lens,     \
+                     static_cast<uint8_t*>(k_pages), static_cast<uint8_t*>(v_pages), scales,    \
+                     block_table, max_blocks_per_seq, cu_seqlens_q, context_lens,               \
                      num_seqs, num_kv_heads, block_size, shift)
   if (head_dim == 128)
     PA_RC8_LAUNCH(128);
@@ -1810,7 +1810,7 @@ extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void*
 }
 
 extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const void* v_pages,
-                                     const float* k_scales, const float* v_scales,
+                                     const float* scales,
                                      const int32_t* block_table, int32_t max_blocks_per_seq,
                                      const int32_t* context_lens, int32_t num_seqs,
                                      int32_t num_q_heads, int32_t num_kv_heads,
@@ -1827,15 +1827,14 @@ extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const v
   if (int rc = check_kinds("paged_attn_decode_fp8", num_tasks, task_kinds, kDecodeKinds))
     return rc;
   if (num_tasks == 0) return pa::clear_error();
-  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !context_lens ||
-      !out || !tasks_dev || (num_combines > 0 && !combines_dev))
+  if (!q || !k_pages || !v_pages || !scales || !block_table || !context_lens || !out ||
+      !tasks_dev || (num_combines > 0 && !combines_dev))
     return pa::set_error(PA_ERR_NULL, "paged_attn_decode_fp8: NULL pointer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, nullptr,
                          context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                          tasks_dev, num_tasks, num_partials, workspace, out);
-  a.k_scales = k_scales;
-  a.v_scales = v_scales;
+  a.scales = scales;
   if (head_dim == 128) {
     hipLaunchKernelGGL(decode_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 128>(combines_dev, num_combines, nullptr, a, st);
@@ -1847,7 +1846,7 @@ extern "C" int paged_attn_decode_fp8(const void* q, const void* k_pages, const v
 }
 
 extern "C" int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_pages,
-                                     const float* k_scales, const float* v_scales,
+                                     const float* scales,
                                      const int32_t* block_table, int32_t max_blocks_per_seq,
                                      const int32_t* cu_seqlens_q, const int32_t* context_lens,
                                      int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
@@ -1867,15 +1866,14 @@ extern "C" int paged_attn_verify_fp8(const void* q, const void* k_pages, const v
     return pa::set_error(PA_ERR_SHAPE, "paged_attn_verify_fp8: %d tokens for %d sequences",
                          num_tokens, num_seqs);
   if (num_tasks == 0) return pa::clear_error();
-  if (!q || !k_pages || !v_pages || !k_scales || !v_scales || !block_table || !cu_seqlens_q ||
-      !context_lens || !out || !tasks_dev || (num_combines > 0 && !combines_dev))
+  if (!q || !k_pages || !v_pages || !scales || !block_table || !cu_seqlens_q || !context_lens ||
+      !out || !tasks_dev || (num_combines > 0 && !combines_dev))
     return pa::set_error(PA_ERR_NULL, "paged_attn_verify_fp8: NULL pointer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                          context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                          tasks_dev, num_tasks, num_partials, workspace, out);
-  a.k_scales = k_scales;
-  a.v_scales = v_scales;
+  a.scales = scales;
   if (head_dim == 128) {
     hipLaunchKernelGGL(decode_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);

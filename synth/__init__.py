@@ -251,7 +251,7 @@ def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinel
 
 def make_fp8_pages(w: Workload, device="cpu", seed: int | None = None, nan_sentinels=True):
     """Draw an fp8 page pool for a workload: uint8 codes [NB, Hkv, bs, D] and float32 page
-    scales [NB, Hkv].
+    scales [NB, Hkv, 2] (the K page's scale, then the V page's).
 
     Codes are uniform over the finite OCP E4M3FN codes (0x00..0x7E with a random sign bit), so
     every magnitude of the format occurs; scales are 2^-e with e uniform in {6, 7, 8} per page.
@@ -288,9 +288,9 @@ def make_fp8_pages(w: Workload, device="cpu", seed: int | None = None, nan_senti
         v_codes.transpose(0, 2, 1, 3)[~valid] = 0x7F
         k_scales[~owned] = np.nan
         v_scales[~owned] = np.nan
+    scales = np.stack([k_scales, v_scales], axis=-1)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
-         for k, v in dict(k_codes=k_codes, v_codes=v_codes, k_scales=k_scales,
-                          v_scales=v_scales).items()}
+         for k, v in dict(k_codes=k_codes, v_codes=v_codes, scales=scales).items()}
     return t
 
 

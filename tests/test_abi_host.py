@@ -236,7 +236,7 @@ def test_launcher_scalar_errors_need_no_gpu():
     p = ctypes.c_void_p(256)
     full = [p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, 0, p, 1, 1, p, 1, 8, p, 1 << 20, p, None]
     assert L.paged_attn_decode(*full) == _abi.PA_ERR_NULL
-    fp8 = full[:3] + [p, p] + full[3:12] + full[13:]
+    fp8 = full[:3] + [p] + full[3:12] + full[13:]     # one scales array after the pages
     assert L.paged_attn_decode_fp8(*fp8) == _abi.PA_ERR_NULL
     # one workgroup per task: 2^23 tasks exceed one launch
     big = list(full)
@@ -246,13 +246,13 @@ def test_launcher_scalar_errors_need_no_gpu():
     rc = L.reshape_and_cache(p, p, p, p, p, 1, p, p, 1, 1 << 23, 1, 1, 64, 16, 0, None)
     assert rc == _abi.PA_ERR_SHAPE
     # the fp8 verify entry: packed rows need cu_seqlens, at least one token per sequence
-    ver = [p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, 1, p, 1, 4, p, 1 << 20,
+    ver = [p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, 1, p, 1, 4, p, 1 << 20,
            p, None]
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_NULL
-    ver[7] = p
-    ver[10] = 1                                           # 1 token for 2 sequences
+    ver[6] = p
+    ver[9] = 1                                            # 1 token for 2 sequences
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_SHAPE
-    ver[10], ver[17] = 4, 0                               # an empty table: a no-op
+    ver[9], ver[16] = 4, 0                                # an empty table: a no-op
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_OK
     v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, 1, nul, 0, 0, nul,
          0, nul, nul]
@@ -274,11 +274,11 @@ def test_attention_entries_refuse_task_kinds_they_do_not_run():
                                    1, 8, p, 1 << 20, p, None)
 
     def decode_fp8(kinds):  # context_lens NULL
-        return L.paged_attn_decode_fp8(p, p, p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, p, 1,
+        return L.paged_attn_decode_fp8(p, p, p, p, p, 1, None, 1, 2, 1, 64, 16, 0.1, p, 1,
                                        kinds, p, 1, 8, p, 1 << 20, p, None)
 
     def verify_fp8(kinds):  # cu_seqlens NULL
-        return L.paged_attn_verify_fp8(p, p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p,
+        return L.paged_attn_verify_fp8(p, p, p, p, p, 1, None, p, 2, 4, 8, 2, 128, 16, 0.1, p,
                                        3, kinds, p, 1, 4, p, 1 << 20, p, None)
 
     def varlen(kinds):      # context_lens NULL

@@ -27,13 +27,14 @@ def _oracle_write(w, vals, pages):
     """The fp8 oracle's cache write on host copies of the inputs."""
     return of.reshape_and_cache_fp8(
         to_np(vals["k_new"]), to_np(vals["v_new"]), pages["k_codes"].cpu().numpy(),
-        pages["v_codes"].cpu().numpy(), pages["k_scales"].cpu().numpy().astype(np.float64),
-        pages["v_scales"].cpu().numpy().astype(np.float64), w.block_table, w.q_lens, w.ctx_lens)
+        pages["v_codes"].cpu().numpy(), pages["scales"][..., 0].cpu().numpy().astype(np.float64),
+        pages["scales"][..., 1].cpu().numpy().astype(np.float64), w.block_table, w.q_lens,
+        w.ctx_lens)
 
 
 def _gpu_write(w, vals, pages, plan):
     plan.write_cache_fp8(vals["k_new"], vals["v_new"], pages["k_codes"], pages["v_codes"],
-                         pages["k_scales"], pages["v_scales"])
+                         pages["scales"])
     torch.cuda.synchronize()
 
 
@@ -41,8 +42,10 @@ def _assert_pages_equal(pages, ref):
     kc, vc, ks, vs = ref
     assert np.array_equal(pages["k_codes"].cpu().numpy(), kc)
     assert np.array_equal(pages["v_codes"].cpu().numpy(), vc)
-    assert np.array_equal(pages["k_scales"].cpu().numpy(), ks.astype(np.float32), equal_nan=True)
-    assert np.array_equal(pages["v_scales"].cpu().numpy(), vs.astype(np.float32), equal_nan=True)
+    # the page scales sit side by side per (block, kv head): K then V
+    got = pages["scales"].cpu().numpy()
+    assert np.array_equal(got[..., 0], ks.astype(np.float32), equal_nan=True)
+    assert np.array_equal(got[..., 1], vs.astype(np.float32), equal_nan=True)
 
 
 @pytest.mark.parametrize("d,bs", [(128, 16), (64, 16), (128, 64), (64, 256)])
@@ -104,8 +107,7 @@ def _decode_case(w, dec_split, seqs=None, **tiling):
     _gpu_write(w, vals, pages, plan)
     out = torch.full_like(vals["q"], float("nan"))
     scale = 1.0 / math.sqrt(w.head_dim)
-    plan.decode_fp8(vals["q"], pages["k_codes"], pages["v_codes"], pages["k_scales"],
-                    pages["v_scales"], scale, out)
+    plan.decode_fp8(vals["q"], pages["k_codes"], pages["v_codes"], pages["scales"], scale, out)
     torch.cuda.synchronize()
     seqs = list(range(w.num_seqs)) if seqs is None else seqs
     kp, table = _subset(kc, ks, w, seqs)
@@ -151,8 +153,7 @@ def _verify_case(w, dec_split, verify_rows, seqs=None):
     _gpu_write(w, vals, pages, plan)
     out = torch.full_like(vals["q"], float("nan"))
     scale = 1.0 / math.sqrt(w.head_dim)
-    plan.verify_fp8(vals["q"], pages["k_codes"], pages["v_codes"], pages["k_scales"],
-                    pages["v_scales"], scale, out)
+    plan.verify_fp8(vals["q"], pages["k_codes"], pages["v_codes"], pages["scales"], scale, out)
     torch.cuda.synchronize()
     seqs = list(range(w.num_seqs)) if seqs is None else seqs
     cu = oa.pack_lengths(w.q_lens)
