@@ -753,6 +753,17 @@ def main():
         "secondary": secondary,
         "context_sweep": sweep,
     }
+    # the metric names two halves: decode GB/s (the headline `value`, per step; the launch in
+    # `roofline`) and prefill TFLOP/s (the packed varlen prefill launch)
+    parts = {"decode": {"workload": args.workload, "launch_gbs": round(achieved, 1),
+                        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}}
+    pf = secondary.get("prefill_varlen_bf16")
+    if pf:
+        parts["prefill"] = {"workload": "prefill_varlen_bf16",
+                            "launch_tflops": pf["attn_tflops_prefill"],
+                            "mfma_frac": pf["mfma_frac"],
+                            "launch_ms_avg": pf["attn_launch_ms_avg"]}
+    line["metric_parts"] = parts
     print(json.dumps(line), flush=True)
 
 
