@@ -104,8 +104,10 @@ def _check(p: Params, cu, ctx):
         raise TaskTableError(ERR_BLOCK_SIZE, "block size must be a power of two in [16, 256]")
     if p.dec_split < 64 or p.dec_split % 64:
         raise TaskTableError(ERR_SHAPE, "dec_split must be a positive multiple of 64")
-    if not 1 <= p.pf_q_tile <= 128:
-        raise TaskTableError(ERR_SHAPE, "pf_q_tile must lie in [1, 128]")
+    # any positive tile height decomposes the rows; how many rows one kernel task can hold is
+    # the library's limit, checked by its own table builder
+    if p.pf_q_tile < 1:
+        raise TaskTableError(ERR_SHAPE, "pf_q_tile must be positive")
     if p.pf_kv_split < 0 or p.pf_kv_split % 64:
         raise TaskTableError(ERR_SHAPE, "pf_kv_split must be 0 or a positive multiple of 64")
     if p.num_workers < 1 or p.decode_weight < 1:

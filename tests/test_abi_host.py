@@ -130,7 +130,7 @@ def test_task_table_errors_match_oracle():
         (dict(hq=2, hkv=1, bs=48), [1], [5], _abi.PA_ERR_BLOCK_SIZE),
         (dict(hq=3, hkv=2, bs=16), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16, dec_split=100), [1], [5], _abi.PA_ERR_SHAPE),
-        (dict(hq=2, hkv=1, bs=16, pf_q_tile=129), [1], [5], _abi.PA_ERR_SHAPE),
+        (dict(hq=2, hkv=1, bs=16, pf_q_tile=0), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16, pf_kv_split=32), [1], [5], _abi.PA_ERR_SHAPE),
         (dict(hq=2, hkv=1, bs=16), [4], [3], _abi.PA_ERR_INPUT),
         (dict(hq=2, hkv=1, bs=16, verify_rows=1), [1], [5], _abi.PA_ERR_SHAPE),
@@ -145,6 +145,14 @@ def test_task_table_errors_match_oracle():
         with pytest.raises(ot.TaskTableError) as e2:
             ot.build_task_table(ot.Params(hq, hkv, 64, bs, **kw), cu, ctx)
         assert e2.value.code == code
+    # the library's tasks hold at most 128 rows (four waves of 32): its builder refuses taller
+    # tiles, which the oracle's decomposition itself would accept
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.build_task_table(pa.make_params(2, 1, 64, 16, pf_q_tile=129), np.array([0, 1], np.int32),
+                            [5])
+    assert e.value.code == _abi.PA_ERR_SHAPE
+    tasks, *_ = ot.build_task_table(ot.Params(2, 1, 64, 16, pf_q_tile=300), [0, 300], [300])
+    assert len(tasks) == 2 and tasks[0][4] == 300      # one tile of 300 rows per head
     # non-increasing offsets are caught by the table builder itself
     with pytest.raises(pa.PagedAttnError) as e:
         pa.build_task_table(pa.make_params(2, 1, 64, 16), np.array([0, 2, 2], np.int32), [5, 5])
