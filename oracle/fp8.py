@@ -23,9 +23,9 @@ import numpy as np
 FP8_MAX = 448.0
 
 
-def decode_e4m3(codes):
-    """Values of E4M3FN codes (uint8 array) as float64; NaN codes give NaN."""
-    c = np.asarray(codes, dtype=np.int64)
+def _e4m3_value(c):
+    """The format's definition of the value of codes c (int array) as float64; NaN codes give
+    NaN."""
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = c & 0x7
@@ -33,6 +33,16 @@ def decode_e4m3(codes):
     sub = (m / 8.0) * 2.0 ** -6
     v = sign * np.where(e == 0, sub, normal)
     return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+# the definition evaluated once for each of the 256 codes
+_VALUES = _e4m3_value(np.arange(256, dtype=np.int64))
+
+
+def decode_e4m3(codes):
+    """Values of E4M3FN codes (uint8 array) as float64; NaN codes give NaN. Each code's value
+    is the definition's (_e4m3_value), looked up, so large page pools decode in one pass."""
+    return _VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 # the 127 finite non-negative values, ascending (codes 0x00 .. 0x7E)
