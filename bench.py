@@ -41,7 +41,7 @@ METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of MFMA peak)"
 HEADLINE = "decode_mha_bf16"
 SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf16", "mixed_bf16",
              "verify_gqa_bf16", "verify_gqa_bf16:as_prefill_tiles", "decode_mha_fp8",
-             "verify_gqa_fp8",
+             "verify_gqa_fp8", "prefill_varlen_fp8", "mixed_fp8",
              "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing",
              "gemm_linear_prefill_qproj", "gemm_linear_mixed_oproj", "gemm_linear_1024x1024x1024",
              "gemm_linear_512x2048x1024", "gemm_linear_2048x512x2048"]
@@ -62,6 +62,9 @@ TILING = {
     # verify batch over fp8 pages
     "decode_mha_fp8": dict(dec_split=1024),
     "verify_gqa_fp8": dict(dec_split=8192, verify_rows=4),
+    # the prefill batch and the mixed step over fp8 pages, through the unified fp8 launch
+    "prefill_varlen_fp8": dict(pf_q_tile=128, pf_kv_split=0),
+    "mixed_fp8": dict(dec_split=4096, pf_q_tile=128, pf_kv_split=0),
     # 8 prompts x 16 decoding requests that alias the prompt's blocks: the prefix is read once
     # per group and kv head; the variant runs the same batch without grouping
     "decode_shared_mha_bf16": dict(dec_split=4096, shared_min=64),
@@ -206,6 +209,9 @@ class Runner:
         self.out = torch.empty_like(self.vals["q"])
         self.scale = 1.0 / math.sqrt(w.head_dim)
         self.decode_only = bool(np.all(w.q_lens == 1))
+        # fp8 tables of decode and verify tasks only go to the verify entry, others (prefill
+        # tiles) to the unified fp8 launch
+        self.verify_kinds = (1 << pa.PA_TASK_DECODE) | (1 << pa.PA_TASK_VERIFY)
         self.work = algorithmic_work(w, self.fp8)
         self.step_no = 0
         self.graphs = None
@@ -256,6 +262,10 @@ class Runner:
             pa.paged_attn_decode_fp8(v["q"], v["k_codes"], v["v_codes"], v["scales"],
                                      self.bt, self.ctx, self.scale, tasks,
                                      self.kinds, combines, nparts, self.ws, self.out)
+        elif self.fp8 and self.kinds & ~self.verify_kinds:
+            pa.paged_attn_varlen_prefill_fp8(v["q"], v["k_codes"], v["v_codes"], v["scales"],
+                                             self.bt, self.cu, self.ctx, self.scale, tasks,
+                                             self.kinds, combines, nparts, self.ws, self.out)
         elif self.fp8:
             pa.paged_attn_verify_fp8(v["q"], v["k_codes"], v["v_codes"], v["scales"],
                                      self.bt, self.cu, self.ctx, self.scale,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 9
+#define PA_ABI_VERSION 10
 
 enum pa_status {
   PA_OK = 0,
@@ -89,15 +89,15 @@ enum pa_task_kind {
  *           PA_TASK_VERIFY: all q_rows (2..16) rows of a short sequence (a speculative draft
  *           being verified; XY-Serve page, section 2.2, "Meta-Attention" serves prefill,
  *           decode and verify alike) for all Hq/Hkv query heads of kv head `head`, keys
- *           [kv0, kv1) minus the causal mask; q_row0 = 0. paged_attn_varlen_prefill and
- *           paged_attn_verify_fp8 run these tasks.
+ *           [kv0, kv1) minus the causal mask; q_row0 = 0. paged_attn_varlen_prefill,
+ *           paged_attn_varlen_prefill_fp8 and paged_attn_verify_fp8 run these tasks.
  *           PA_TASK_SHARED: keys [kv0, kv1) of a prefix that q_rows consecutive decode
  *           sequences seq .. seq+q_rows-1 hold in the same physical blocks (XY-Serve page,
  *           automatic prefix cache; ATB page, KV cache reuse), for their single query rows and
  *           all Hq/Hkv query heads of kv head `head`: the pages are read once for all of them.
  *           Always writes partials: member i, head j goes to row partial + i*q_row0 + j (q_row0
- *           holds the member stride). paged_attn_decode, paged_attn_varlen_prefill and
- *           paged_attn_decode_fp8 run these tasks.
+ *           holds the member stride). paged_attn_decode, paged_attn_varlen_prefill,
+ *           paged_attn_varlen_prefill_fp8 and paged_attn_decode_fp8 run these tasks.
  *   partial -1: the task sees all keys its rows need and writes `out` directly.
  *           >= 0: first workspace row of this task's partial result (one row per
  *           (query row, head) pair it covers); split_combine merges the partials. */
@@ -353,6 +353,27 @@ int paged_attn_verify_fp8(const void* q, const void* k_pages, const void* v_page
                           uint32_t task_kinds, const pa_combine* combines_dev,
                           int32_t num_combines, int32_t num_partials, void* workspace,
                           size_t workspace_bytes, void* out, void* stream);
+
+/* The unified launch over fp8 pages (cann-recipes-infer page, section 3.3, the packed
+ * variable-length call over paged prefixes; section 5.2, values read as code times their page's
+ * scale): as paged_attn_varlen_prefill with dtype PA_BF16 for q and out, any mix of decode,
+ * prefill, verify and shared-prefix tasks in one grid, over the pages and scales of
+ * paged_attn_decode_fp8. Prefill tasks convert each K/V tile to bf16 (exactly: codes times a
+ * power-of-two scale) on its way into LDS and then run the bf16 MFMA tile path; the other
+ * kinds run the fp8 decode path. task_kinds may hold every kind.
+ *   Device pointers: q, k_pages, v_pages, scales, block_table, cu_seqlens_q, context_lens,
+ *   tasks_dev, combines_dev, workspace, out.
+ *   Errors as paged_attn_varlen_prefill. */
+int paged_attn_varlen_prefill_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                  const float* scales, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, float scale,
+                                  const pa_task* tasks_dev, int32_t num_tasks,
+                                  uint32_t task_kinds, const pa_combine* combines_dev,
+                                  int32_t num_combines, int32_t num_partials, void* workspace,
+                                  size_t workspace_bytes, void* out, void* stream);
 
 /* Debug check of a host copy of a block table (cann-recipes-infer page, section 4.4, first
  * check: page ids inside [0, max_pages)): every entry a sequence needs,

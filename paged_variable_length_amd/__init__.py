@@ -28,13 +28,14 @@ import numpy as np
 
 from . import _abi
 from ._abi import (PA_BF16, PA_FP32, PA_TASK_DECODE, PA_TASK_PREFILL,  # noqa: F401
-                   PA_TASK_VERIFY, PagedAttnError, PaCombine, PaGemmParams, PaGemmReduce,
-                   PaGemmTask, PaParams, PaTask, check, lib)
+                   PA_TASK_VERIFY, PA_TASK_SHARED, PagedAttnError, PaCombine, PaGemmParams,
+                   PaGemmReduce, PaGemmTask, PaParams, PaTask, check, lib)
 
 __all__ = ["pack_seqlens", "build_task_table", "workspace_bytes", "reshape_and_cache",
            "paged_attn_decode", "paged_attn_varlen_prefill", "paged_attn_varlen_prefill_noalloc",
            "validate_block_table",
            "reshape_and_cache_fp8", "paged_attn_decode_fp8", "paged_attn_verify_fp8",
+           "paged_attn_varlen_prefill_fp8",
            "TaskTable", "StepPlan", "make_params", "PagedAttnError", "PA_BF16", "PA_FP32",
            "build_gemm_table", "gemm_workspace_bytes", "smooth_gemm", "GemmTable", "GemmPlan"]
 
@@ -292,12 +293,10 @@ def paged_attn_decode_fp8(q, k_pages, v_pages, scales, block_table, context_lens
     check(lib().paged_attn_decode_fp8(*args), "paged_attn_decode_fp8")
 
 
-def paged_attn_verify_fp8(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
-                          context_lens, scale, tasks_dev, task_kinds, combines_dev, num_partials,
-                          workspace, out, stream=None):
-    """Decode rows and speculative drafts over fp8 pages with page scales (library kernels).
-    q/out bf16 [T, Hq, D] packed by cu_seqlens_q; pages uint8 [NB, Hkv, bs, D]; scales
-    float32 [NB, Hkv]. Runs the table's decode and verify tasks only."""
+def _fp8_packed_args(q, k_pages, v_pages, scales, block_table, cu_seqlens_q, context_lens,
+                     scale, tasks_dev, task_kinds, combines_dev, num_partials, workspace, out,
+                     stream):
+    """Argument list of the fp8 entries over packed rows (verify and the unified launch)."""
     torch = _torch()
     if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
         raise ValueError("k_pages and v_pages must both be [NB, Hkv, bs, D]")
@@ -318,7 +317,31 @@ def paged_attn_verify_fp8(q, k_pages, v_pages, scales, block_table, cu_seqlens_q
             float(scale)] + \
         _table_args(tasks_dev, task_kinds, combines_dev, num_partials, workspace) + \
         [_dev(out, "out", torch.bfloat16), _stream(stream)]
+    return args
+
+
+def paged_attn_verify_fp8(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
+                          context_lens, scale, tasks_dev, task_kinds, combines_dev, num_partials,
+                          workspace, out, stream=None):
+    """Decode rows and speculative drafts over fp8 pages with page scales (library kernels).
+    q/out bf16 [T, Hq, D] packed by cu_seqlens_q; pages uint8 [NB, Hkv, bs, D]; scales
+    float32 [NB, Hkv, 2]. Runs the table's decode and verify tasks only."""
+    args = _fp8_packed_args(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
+                            context_lens, scale, tasks_dev, task_kinds, combines_dev,
+                            num_partials, workspace, out, stream)
     check(lib().paged_attn_verify_fp8(*args), "paged_attn_verify_fp8")
+
+
+def paged_attn_varlen_prefill_fp8(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
+                                  context_lens, scale, tasks_dev, task_kinds, combines_dev,
+                                  num_partials, workspace, out, stream=None):
+    """The unified launch over fp8 pages (library kernels): decode, prefill, verify and
+    shared-prefix tasks in one grid. q/out bf16 [T, Hq, D] packed by cu_seqlens_q; pages uint8
+    [NB, Hkv, bs, D]; scales float32 [NB, Hkv, 2]."""
+    args = _fp8_packed_args(q, k_pages, v_pages, scales, block_table, cu_seqlens_q,
+                            context_lens, scale, tasks_dev, task_kinds, combines_dev,
+                            num_partials, workspace, out, stream)
+    check(lib().paged_attn_varlen_prefill_fp8(*args), "paged_attn_varlen_prefill_fp8")
 
 
 def paged_attn_varlen_prefill(q, k_pages, v_pages, block_table, cu_seqlens_q, context_lens,
@@ -428,6 +451,12 @@ class StepPlan:
         paged_attn_varlen_prefill(q, k_pages, v_pages, self.block_table, self.cu, self.ctx,
                                   scale, self.tasks, self.table.kinds, self.combines,
                                   self.num_partials, self.workspace, out, stream)
+
+    def varlen_fp8(self, q, k_pages, v_pages, scales, scale, out, stream=None):
+        paged_attn_varlen_prefill_fp8(q, k_pages, v_pages, scales, self.block_table, self.cu,
+                                      self.ctx, scale, self.tasks, self.table.kinds,
+                                      self.combines, self.num_partials, self.workspace, out,
+                                      stream)
 
 
 # ------------------------------------------------------------------ SmoothGEMM

@@ -27,7 +27,7 @@ PA_TASK_VERIFY = 2
 PA_TASK_SHARED = 3
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
 ALL_KINDS = 0xF          # PA_KIND_BIT of every task kind
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 ERROR_NAMES = {
     PA_ERR_NULL: "PA_ERR_NULL", PA_ERR_SHAPE: "PA_ERR_SHAPE",
@@ -39,7 +39,8 @@ ERROR_NAMES = {
 EXPORTS = ("pa_abi_version", "pa_last_error", "pa_pack_seqlens", "build_task_table",
            "pa_workspace_bytes", "reshape_and_cache", "paged_attn_decode",
            "paged_attn_varlen_prefill", "pa_validate_block_table", "reshape_and_cache_fp8",
-           "paged_attn_decode_fp8", "paged_attn_verify_fp8", "paged_attn_varlen_prefill_noalloc",
+           "paged_attn_decode_fp8", "paged_attn_verify_fp8", "paged_attn_varlen_prefill_fp8",
+           "paged_attn_varlen_prefill_noalloc",
            "build_task_table_shared", "build_gemm_table", "pa_gemm_workspace_bytes",
            "smooth_gemm")
 
@@ -140,6 +141,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_verify_fp8.argtypes = [p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
                                         i32, ctypes.c_float, p, i32, u32, p, i32, i32, p,
                                         ctypes.c_size_t, p, p]
+    # same argument list as the verify entry
+    L.paged_attn_varlen_prefill_fp8.restype = ctypes.c_int
+    L.paged_attn_varlen_prefill_fp8.argtypes = list(L.paged_attn_verify_fp8.argtypes)
     L.pa_validate_block_table.restype = ctypes.c_int
     L.pa_validate_block_table.argtypes = [pi32, i32, pi32, i32, i32, i32]
     L.build_gemm_table.restype = ctypes.c_int

@@ -756,6 +756,7 @@ __device__ __forceinline__ void lds_wait(T (&r)[4]) {
 }
 
 typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(4))) const float cfloat;
 
 // Causal mask of one 32-key block of S^T scores: register r holds key offset
 // BASE + 8*(r/4) + r%4 (plus the lane's own offset, folded into lim); offsets >= lim become
@@ -781,7 +782,12 @@ __device__ __forceinline__ void mask_block(f32x16& s, int lim) {
   s[14] = mask_one<BASE + 26>(s[14], lim, ninf); s[15] = mask_one<BASE + 27>(s[15], lim, ninf);
 }
 
-template <int D>
+// FP8: the pages hold E4M3FN codes with a power-of-two scale per page and tensor. A wave then
+// loads its share of a tile into registers (8 codes per lane and piece, the same elements the
+// direct load would move), and after the tile's compute converts them exactly to bf16 and
+// writes them where the direct load would have put them: the LDS layout, the buffers and the
+// compute are those of the bf16 pages.
+template <int D, bool FP8 = false>
 __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   typedef PrefillCfg<D> C;
   constexpr int KS = D / 16;   // k-steps of the QK product
@@ -822,10 +828,11 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     }
   }
 
+  constexpr int EB = FP8 ? 1 : 2;           // bytes per element in the pages
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
-  const char* kbase = static_cast<const char*>(a.k_pages) + kvh * head_stride * 2;
-  const char* vbase = static_cast<const char*>(a.v_pages) + kvh * head_stride * 2;
+  const char* kbase = static_cast<const char*>(a.k_pages) + kvh * head_stride * EB;
+  const char* vbase = static_cast<const char*>(a.v_pages) + kvh * head_stride * EB;
   cint32* bt = (cint32*)(a.block_table + static_cast<size_t>(s) * a.max_blocks);
 
   // ---- LDS: [K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1], one 64-key tile each.
@@ -868,15 +875,32 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     const int kp = min(kv0 + tile * C::kTile + wave_u * P * C::kKeysPerLoad, kv1 - 1);
     return bt[kp >> a.bs_shift];
   };
+  // fp8 staging: codes of the K (0) and V (1) pieces in flight, and their pages' scales
+  u32x2 stage[2][P];
+  float stage_sc[2] = {0.f, 0.f};
   // Keys past kv1 (last tile only) are read from key kv1-1 instead (valid memory, finite
   // values); they are masked in the scores. `which` 0 loads K into K buffer `buf`, 1 loads V.
+  // The fp8 form of an element sits at half the byte offset of its bf16 form.
   auto issue = [&](int tile, int id, int which, int buf) {
     const int ts = kv0 + tile * C::kTile;
     const bool full = ts + C::kTile <= kv1;
-    const char* page = (which ? vbase : kbase) + static_cast<size_t>(id) * block_stride * 2;
+    const char* page = (which ? vbase : kbase) + static_cast<size_t>(id) * block_stride * EB;
     char* dst0 = smem + (2 * which + buf) * C::kTileBytes + wave_u * P * 1024;
     const uint32_t tile_slot = static_cast<uint32_t>(ts & (bs - 1)) * C::kRowBytes;
-    if (full) {
+    if constexpr (FP8) {
+      stage_sc[which] = ((cfloat*)a.scales)[2 * (static_cast<size_t>(id) * a.num_kv_heads + kvh) + which];
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        uint32_t off;
+        if (full) {
+          off = tile_slot + dma_off(i) + i * 1024;
+        } else {
+          const int kabs = min(ts + key0 + i * C::kKeysPerLoad, kv1 - 1);
+          off = (kabs & (bs - 1)) * C::kRowBytes + (dma_off(i) & (C::kRowBytes - 1));
+        }
+        stage[which][i] = *reinterpret_cast<const u32x2*>(page + off / 2);
+      }
+    } else if (full) {
 #pragma unroll
       for (int i = 0; i < P; ++i)
         __builtin_amdgcn_global_load_lds(page + tile_slot + dma_off(i) + i * 1024,
@@ -889,6 +913,21 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         __builtin_amdgcn_global_load_lds(
             page + (kabs & (bs - 1)) * C::kRowBytes + (dma_off(i) & (C::kRowBytes - 1)),
             (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16, 0, 0);
+      }
+    }
+  };
+  // fp8: converts the staged codes of `which` and writes them to LDS buffer `buf`, each lane
+  // at the position its direct load would have written (16 bytes per lane and piece)
+  auto commit = [&](int which, int buf) {
+    if constexpr (FP8) {
+      char* dst = smem + (2 * which + buf) * C::kTileBytes + wave_u * P * 1024 + 16 * lane;
+      const float sc = stage_sc[which];
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const u32x2 w = stage[which][i];
+        *reinterpret_cast<u32x4*>(dst + i * 1024) =
+            u32x4{fp8x2_to_bf16x2<false>(w[0], sc), fp8x2_to_bf16x2<true>(w[0], sc),
+                  fp8x2_to_bf16x2<false>(w[1], sc), fp8x2_to_bf16x2<true>(w[1], sc)};
       }
     }
   };
@@ -1123,9 +1162,14 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     const int id0 = block_id(0);
     issue(0, id0, 0, 0);
     issue(0, id0, 1, 0);
+    commit(0, 0);
+    commit(1, 0);
   }
   int idV = block_id(1);                    // tile j+1 (its V is loaded in iteration j)
-  if (ntiles > 1) issue(1, idV, 0, 1);
+  if (ntiles > 1) {
+    issue(1, idV, 0, 1);
+    commit(0, 1);
+  }
   int idK = block_id(2);                    // tile j+2 (its K is loaded in iteration j)
   int idN = block_id(3);                    // tile j+3, read one iteration ahead
   __builtin_amdgcn_s_waitcnt(0);
@@ -1176,6 +1220,10 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       l += psum;
       phase_b(std::integral_constant<int, PAR>(), T_(), F_(), snext, kv0 + (j + 1) * C::kTile);
     }
+    // fp8: the tiles loaded above reach their buffers (free since this iteration's barrier)
+    // before the next iteration's barrier
+    if (j + 2 < ntiles) commit(0, PAR);
+    if (j + 1 < ntiles) commit(1, 1 - PAR);
   };
   for (int j = 0; j < ntiles; j += 2) {
     iteration(j, I0(), sa, sb);
@@ -1258,6 +1306,19 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
     prefill_task<D>(a, t, smem);
   else
     decode_task_bf16<D>(a, t, reinterpret_cast<float*>(smem));
+}
+
+// The unified launch over fp8 pages: every task kind, rows addressed through cu_seqlens.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) {
+  constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
+  constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
+  __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
+  const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
+  if (t.kind == PA_TASK_PREFILL)
+    prefill_task<D, true>(a, t, smem);
+  else
+    decode_task_fp8<D>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // One workgroup per combine record; each wave merges one (row, head) at a time.
@@ -1656,17 +1717,23 @@ int varlen_enqueue(const char* who, const void* q, const void* k_pages, const vo
                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, float scale, const pa_task* tasks_dev, int32_t num_tasks,
                    const pa_combine* combines_dev, int32_t num_combines, int32_t num_partials,
-                   void* workspace, void* out, void* stream) {
+                   void* workspace, void* out, void* stream, const float* scales = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq,
-                               cu_seqlens_q, context_lens, num_q_heads, num_kv_heads, head_dim,
-                               block_size, scale, tasks_dev, num_tasks, num_partials, workspace,
-                               out);
+  AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
+                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                         tasks_dev, num_tasks, num_partials, workspace, out);
+  a.scales = scales;  // fp8 pages when set
   if (head_dim == 128) {
-    hipLaunchKernelGGL(meta_attn_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    if (scales)
+      hipLaunchKernelGGL(meta_attn_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(meta_attn_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
   } else {
-    hipLaunchKernelGGL(meta_attn_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    if (scales)
+      hipLaunchKernelGGL(meta_attn_fp8_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(meta_attn_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
   }
   return hip_check(who);
@@ -1882,4 +1949,29 @@ extern "C" int paged_attn_verify_fp8(const void* q, const void* k_pages, const v
     launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
   }
   return hip_check("paged_attn_verify_fp8");
+}
+
+extern "C" int paged_attn_varlen_prefill_fp8(
+    const void* q, const void* k_pages, const void* v_pages, const float* scales,
+    const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    const pa_task* tasks_dev, int32_t num_tasks, uint32_t task_kinds,
+    const pa_combine* combines_dev, int32_t num_combines, int32_t num_partials, void* workspace,
+    size_t workspace_bytes, void* out, void* stream) {
+  const char* who = "paged_attn_varlen_prefill_fp8";
+  if (int rc = varlen_checks(who, q, k_pages, v_pages, block_table, max_blocks_per_seq,
+                             cu_seqlens_q, context_lens, num_seqs, num_tokens, num_q_heads,
+                             num_kv_heads, head_dim, block_size, PA_BF16, tasks_dev, num_tasks,
+                             task_kinds, combines_dev, num_combines, num_partials, out))
+    return rc;
+  if (int rc = check_workspace(who, num_partials, num_combines, head_dim, workspace_bytes,
+                               workspace))
+    return rc;
+  if (num_tasks == 0) return pa::clear_error();
+  if (!scales) return pa::set_error(PA_ERR_NULL, "%s: NULL pointer", who);
+  return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
+                        context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                        tasks_dev, num_tasks, combines_dev, num_combines, num_partials,
+                        workspace, out, stream, scales);
 }

@@ -92,13 +92,15 @@ def _lengths(name: str, rng: np.random.Generator):
         ctx = np.clip(np.floor(np.exp(u)), 64, 32768).astype(np.int64)
         bs = 16 if name.endswith("bs16") else 64
         return np.ones(256, np.int64), ctx, 32, 8, 128, bs, "bf16", None
-    if name == "prefill_varlen_bf16":
+    if name in ("prefill_varlen_bf16", "prefill_varlen_fp8"):
+        # (the fp8 variant has the same lengths, over fp8 pages with per-page scales)
         comp = rng.choice(3, size=16, p=[0.6, 0.25, 0.15])
         lo = np.array([10, 1000, 10000])
         hi = np.array([50, 5000, 20000])
         lens = np.array([rng.integers(lo[c], hi[c] + 1) for c in comp], dtype=np.int64)
         return lens.copy(), lens.copy(), 32, 8, 128, 16, "bf16", None
-    if name == "mixed_bf16":
+    if name in ("mixed_bf16", "mixed_fp8"):
+        # (the fp8 variant has the same lengths, over fp8 pages with per-page scales)
         dec_ctx = rng.integers(256, 32769, size=200).astype(np.int64)
         prefix = rng.integers(0, 131073, size=4).astype(np.int64)
         q = np.concatenate([np.ones(200, np.int64), np.full(4, 512, np.int64)])
@@ -125,7 +127,9 @@ WORKLOADS = {
     "decode_gqa_bf16_bs16": 3,
     "decode_gqa_bf16_bs64": 3,
     "prefill_varlen_bf16": 4,
+    "prefill_varlen_fp8": 4,
     "mixed_bf16": 5,
+    "mixed_fp8": 5,
     "verify_gqa_bf16": 6,
     "verify_gqa_fp8": 6,
     "decode_mha_fp8": 2,
@@ -233,15 +237,7 @@ def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinel
     k_pages = draw(nb, hkv, bs, d)
     v_pages = draw(nb, hkv, bs, d)
     if nan_sentinels:
-        valid = np.zeros((nb, bs), dtype=bool)
-        for s in range(w.num_seqs):
-            prefix = int(w.ctx_lens[s] - w.q_lens[s])      # slots already cached
-            nblk = (int(w.ctx_lens[s]) + bs - 1) // bs
-            for j in range(nblk):
-                b = int(w.block_table[s, j])
-                lo, hi = j * bs, min((j + 1) * bs, prefix)
-                if hi > lo:
-                    valid[b, : hi - lo] = True
+        valid, _ = _cached_slots(w)
         mask = torch.from_numpy(~valid).to(device)
         # [NB, bs] mask over the [NB, bs] leading dims of the (block, slot, head, dim) view
         k_pages.transpose(1, 2)[mask] = float("nan")
@@ -250,48 +246,57 @@ def make_values(w: Workload, device="cpu", seed: int | None = None, nan_sentinel
 
 
 def make_fp8_pages(w: Workload, device="cpu", seed: int | None = None, nan_sentinels=True):
-    """Draw an fp8 page pool for a workload: uint8 codes [NB, Hkv, bs, D] and float32 page
-    scales [NB, Hkv, 2] (the K page's scale, then the V page's).
+    """Draw an fp8 page pool for a workload with a seeded torch generator on ``device``: uint8
+    codes [NB, Hkv, bs, D] and float32 page scales [NB, Hkv, 2] (the K page's scale, then the
+    V page's).
 
-    Codes are uniform over the finite OCP E4M3FN codes (0x00..0x7E with a random sign bit), so
-    every magnitude of the format occurs; scales are 2^-e with e uniform in {6, 7, 8} per page.
-    Nothing here encodes values: the codes are drawn directly. With ``nan_sentinels`` every slot
-    that holds no cached key (as in make_values) holds the NaN code 0x7F, and the scales of
-    blocks no sequence owns are NaN.
+    Codes are uniform over the finite OCP E4M3FN codes (magnitude 0x00..0x7E, then a random
+    sign bit), so every magnitude of the format occurs; scales are 2^-e with e uniform in
+    {6, 7, 8} per page. Nothing here encodes values: the codes are drawn directly. With
+    ``nan_sentinels`` every slot that holds no cached key (as in make_values) holds the NaN
+    code 0x7F, and the scales of blocks no sequence owns are NaN.
     """
     import torch
     seed = (w.seed if seed is None else seed) + 7919
-    rng = np.random.default_rng(seed)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
     hkv, d, bs, nb = w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks
 
     def codes():
-        mag = rng.integers(0, 0x7F, size=(nb, hkv, bs, d), dtype=np.uint8)
-        sign = (rng.integers(0, 2, size=(nb, hkv, bs, d), dtype=np.uint8) << 7).astype(np.uint8)
-        return mag | sign
+        mag = torch.randint(0, 0x7F, (nb, hkv, bs, d), generator=g, device=device,
+                            dtype=torch.uint8)
+        sign = torch.randint(0, 2, (nb, hkv, bs, d), generator=g, device=device,
+                             dtype=torch.uint8)
+        return mag | (sign << 7)
 
     k_codes, v_codes = codes(), codes()
-    k_scales = np.exp2(-rng.integers(6, 9, size=(nb, hkv))).astype(np.float32)
-    v_scales = np.exp2(-rng.integers(6, 9, size=(nb, hkv))).astype(np.float32)
+    e = torch.randint(6, 9, (nb, hkv, 2), generator=g, device=device, dtype=torch.int32)
+    scales = torch.exp2(-e.to(torch.float32))
     if nan_sentinels:
-        valid = np.zeros((nb, bs), dtype=bool)
-        owned = np.zeros(nb, dtype=bool)
-        for s in range(w.num_seqs):
-            prefix = int(w.ctx_lens[s] - w.q_lens[s])
-            nblk = (int(w.ctx_lens[s]) + bs - 1) // bs
-            for j in range(nblk):
-                b = int(w.block_table[s, j])
-                owned[b] = True
-                lo, hi = j * bs, min((j + 1) * bs, prefix)
-                if hi > lo:
-                    valid[b, : hi - lo] = True
-        k_codes.transpose(0, 2, 1, 3)[~valid] = 0x7F
-        v_codes.transpose(0, 2, 1, 3)[~valid] = 0x7F
-        k_scales[~owned] = np.nan
-        v_scales[~owned] = np.nan
-    scales = np.stack([k_scales, v_scales], axis=-1)
-    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
-         for k, v in dict(k_codes=k_codes, v_codes=v_codes, scales=scales).items()}
-    return t
+        valid, owned = _cached_slots(w)
+        mask = torch.from_numpy(~valid).to(device)
+        k_codes.transpose(1, 2)[mask] = 0x7F
+        v_codes.transpose(1, 2)[mask] = 0x7F
+        scales[torch.from_numpy(~owned).to(device)] = float("nan")
+    return dict(k_codes=k_codes, v_codes=v_codes, scales=scales)
+
+
+def _cached_slots(w: Workload):
+    """valid [NB, bs]: slots that hold a key cached before this step; owned [NB]: blocks some
+    sequence's table lists."""
+    bs = w.block_size
+    valid = np.zeros((w.num_blocks, bs), dtype=bool)
+    owned = np.zeros(w.num_blocks, dtype=bool)
+    for s in range(w.num_seqs):
+        prefix = int(w.ctx_lens[s] - w.q_lens[s])      # slots already cached
+        nblk = (int(w.ctx_lens[s]) + bs - 1) // bs
+        for j in range(nblk):
+            b = int(w.block_table[s, j])
+            owned[b] = True
+            lo, hi = j * bs, min((j + 1) * bs, prefix)
+            if hi > lo:
+                valid[b, : hi - lo] = True
+    return valid, owned
 
 
 # ---------------------------------------------------------------- Linear (SmoothGEMM) inputs

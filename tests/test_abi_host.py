@@ -262,6 +262,22 @@ def test_launcher_scalar_errors_need_no_gpu():
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_ERR_SHAPE
     ver[9], ver[16] = 4, 0                                # an empty table: a no-op
     assert L.paged_attn_verify_fp8(*ver) == _abi.PA_OK
+    # the fp8 unified launch takes the verify entry's argument list and its checks, plus the
+    # scales array: every other pointer given, scales NULL
+    uni = [p, p, p, None, p, 1, p, p, 2, 4, 8, 2, 128, 16, 0.1, p, 3, 0xF, p, 1, 4, p, 1 << 20,
+           p, None]
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_ERR_NULL
+    uni[3], uni[9] = p, 1                                 # 1 token for 2 sequences
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_ERR_SHAPE
+    uni[9], uni[12] = 4, 96                               # head_dim 96
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_ERR_SHAPE
+    uni[12], uni[13] = 128, 24                            # block size 24
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_ERR_BLOCK_SIZE
+    uni[13], uni[21] = 16, None                           # partial rows without a workspace
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_ERR_NULL
+    assert b"workspace" in L.pa_last_error()
+    uni[21], uni[16] = p, 0                               # an empty table: a no-op
+    assert L.paged_attn_varlen_prefill_fp8(*uni) == _abi.PA_OK
     v = [nul, nul, nul, nul, 1, nul, nul, 1, 1, 2, 1, 64, 16, 0.1, 1, nul, 1, 1, nul, 0, 0, nul,
          0, nul, nul]
     assert L.paged_attn_varlen_prefill(*v) == _abi.PA_ERR_DTYPE                  # fp32 prefill
@@ -293,8 +309,12 @@ def test_attention_entries_refuse_task_kinds_they_do_not_run():
         return L.paged_attn_varlen_prefill(p, p, p, p, 1, p, None, 1, 2, 2, 1, 64, 16, 0.1, 0, p,
                                            1, kinds, p, 1, 8, p, 1 << 20, p, None)
 
+    def varlen_fp8(kinds):  # context_lens NULL
+        return L.paged_attn_varlen_prefill_fp8(p, p, p, p, p, 1, p, None, 1, 2, 2, 1, 64, 16, 0.1,
+                                               p, 1, kinds, p, 1, 8, p, 1 << 20, p, None)
+
     cases = [(decode, DEC | SHA), (decode_fp8, DEC | SHA), (verify_fp8, DEC | VER),
-             (varlen, DEC | PRE | VER | SHA)]
+             (varlen, DEC | PRE | VER | SHA), (varlen_fp8, DEC | PRE | VER | SHA)]
     for fn, allowed in cases:
         for kinds in range(1, 16):
             rc = fn(kinds)
