@@ -916,20 +916,30 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       }
     }
   };
-  // fp8: converts the staged codes of `which` and writes them to LDS buffer `buf`, each lane
-  // at the position its direct load would have written (16 bytes per lane and piece)
-  auto commit = [&](int which, int buf) {
+  // fp8: converts the staged codes of piece i of `which` and writes them to LDS buffer `buf`,
+  // each lane at the position its direct load would have written (16 bytes per lane)
+  auto commit_piece = [&](int which, int buf, int i) {
     if constexpr (FP8) {
       char* dst = smem + (2 * which + buf) * C::kTileBytes + wave_u * P * 1024 + 16 * lane;
       const float sc = stage_sc[which];
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const u32x2 w = stage[which][i];
-        *reinterpret_cast<u32x4*>(dst + i * 1024) =
-            u32x4{fp8x2_to_bf16x2<false>(w[0], sc), fp8x2_to_bf16x2<true>(w[0], sc),
-                  fp8x2_to_bf16x2<false>(w[1], sc), fp8x2_to_bf16x2<true>(w[1], sc)};
-      }
+      const u32x2 w = stage[which][i];
+      *reinterpret_cast<u32x4*>(dst + i * 1024) =
+          u32x4{fp8x2_to_bf16x2<false>(w[0], sc), fp8x2_to_bf16x2<true>(w[0], sc),
+                fp8x2_to_bf16x2<false>(w[1], sc), fp8x2_to_bf16x2<true>(w[1], sc)};
     }
+  };
+  auto commit = [&](int which, int buf) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) commit_piece(which, buf, i);
+  };
+  // fp8: a barrier that waits for this wave's LDS operations only (lgkmcnt; vmcnt and expcnt
+  // not waited for), so register loads stay in flight; the empty asm statements keep the
+  // compiler from moving LDS accesses across it
+  auto lds_barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   f32x16 acc[NB];
@@ -1088,7 +1098,9 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   // Phase B: value product of the current tile (V buffer VB) with pw, and the causal mask of
   // the next tile's scores sn (starting at key ts_next); with MAX also the maximum of sn and
   // the rescale to it (the wave's first tile only).
-  auto phase_b = [&](auto vb_tag, auto do_pv, auto do_max, f32x16 (&sn)[2], int ts_next) {
+  // `hook(kk)` runs after the matrix steps of k-step kk (fp8: a share of the tile conversions).
+  auto phase_b = [&](auto vb_tag, auto do_pv, auto do_max, f32x16 (&sn)[2], int ts_next,
+                     auto hook) {
     constexpr int VOFF = decltype(vb_tag)::value * C::kTileBytes;
     constexpr bool PV = decltype(do_pv)::value, MAX = decltype(do_max)::value;
     typedef u32x2 VR[NR];
@@ -1134,18 +1146,22 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       lds_wait<NR>(vr0);
     }
     pv(0, vr0);
+    hook(0);
     if constexpr (PV) {
       v_issue(std::integral_constant<int, 2>(), vr0);
       lds_wait<NR>(vr1);
     }
     pv(1, vr1);
+    hook(1);
     if constexpr (PV) {
       v_issue(std::integral_constant<int, 3>(), vr1);
       lds_wait<NR>(vr0);
     }
     pv(2, vr0);
+    hook(2);
     if constexpr (PV) lds_wait<0>(vr1);
     pv(3, vr1);
+    hook(3);
     if constexpr (MAX) {
       // the first tile: its exact maximum becomes the reference (acc and l are still zero)
       m = fmaxf(mx, wave_shfl_xor(mx, 32)) * c;
@@ -1172,12 +1188,19 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   }
   int idK = block_id(2);                    // tile j+2 (its K is loaded in iteration j)
   int idN = block_id(3);                    // tile j+3, read one iteration ahead
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if constexpr (FP8) {
+    // the codes iteration 0 converts: K(2) and V(1)
+    if (ntiles > 2) issue(2, idK, 0, 0);
+    if (ntiles > 1) issue(1, idV, 1, 0);
+    lds_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   if (nw > 0) {
     float unused;
     phase_a(I0(), T_(), F_(), sa, sb, unused);
-    phase_b(I0(), F_(), T_(), sa, kv0);
+    phase_b(I0(), F_(), T_(), sa, kv0, [](int) {});
   }
 
   // ---- iteration j: wait for K(j+1) and V(j); load K(j+2) and V(j+1) into the buffers the
@@ -1195,20 +1218,48 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   // in iteration j-1 can be overwritten. Iteration 0 overwrites K buffer 0, whose tile 0 the
   // prologue read, so it needs that barrier too whenever it issues K(2) (a wave with no tile
   // to compute skips the prologue's reads and would otherwise reach the issue first).
+  //
+  // fp8 pages: the buffers and their reads are the same; what changes is how a tile gets
+  // there. The codes of K(t) are loaded into registers at the end of iteration t-3 (for t = 2:
+  // in the prologue) and converted and written to K buffer t%2 during the value product of
+  // iteration t-2; those of V(t) are loaded at the end of iteration t-2 and written during
+  // iteration t-1. These are ordinary LDS writes, so a wave passes the barrier after
+  // s_waitcnt lgkmcnt(0) alone: its writes are in LDS (a) and its reads have returned (b), while
+  // its register loads for the next conversions stay in flight across the barrier.
   auto iteration = [&](int j, auto par_tag, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
     constexpr int PAR = decltype(par_tag)::value;
     // opaque redefinition: values derived from these bases (the per-k-step and per-piece
     // addresses) are then recomputed where used instead of held in registers across the loop
     asm volatile("" : "+v"(ka0), "+v"(dma0));
     if (j > 0 || ntiles > 2) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      if constexpr (FP8) {
+        lds_barrier();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
     }
-    if (j + 2 < ntiles) issue(j + 2, idK, 0, PAR);
-    if (j + 1 < ntiles) issue(j + 1, idV, 1, 1 - PAR);
+    if constexpr (!FP8) {
+      if (j + 2 < ntiles) issue(j + 2, idK, 0, PAR);
+      if (j + 1 < ntiles) issue(j + 1, idV, 1, 1 - PAR);
+    }
     idV = idK;
     idK = idN;
     idN = block_id(j + 4);
+    // fp8: K(j+2) and V(j+1), staged in registers, go to their buffers in shares after the
+    // value product's k-steps (P/2 pieces each), or all at once on a wave with nothing to
+    // compute
+    const bool k_due = j + 2 < ntiles, v_due = j + 1 < ntiles;
+    auto convert_share = [&](int kk) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int q = 0; q < P / 2; ++q) {
+          const int item = kk * (P / 2) + q;
+          const int which = item / P, i = item % P;
+          if (which == 0 ? k_due : v_due) commit_piece(which, which ? 1 - PAR : PAR, i);
+        }
+      }
+    };
     // The scores of tile j+1 are formed even when this wave has no key to see there (its
     // last tile, or past the range): the mask then sets all of them to -inf, whatever the K
     // buffer holds, and their weights are zero. One code path keeps the accumulators in
@@ -1218,12 +1269,17 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       phase_a(std::integral_constant<int, 1 - PAR>(), T_(), T_(), snext, scur, psum);
       if (__builtin_amdgcn_ballot_w64(!(psum <= 65536.f)) != 0) retake(scur, psum);
       l += psum;
-      phase_b(std::integral_constant<int, PAR>(), T_(), F_(), snext, kv0 + (j + 1) * C::kTile);
+      phase_b(std::integral_constant<int, PAR>(), T_(), F_(), snext, kv0 + (j + 1) * C::kTile,
+              convert_share);
+    } else if constexpr (FP8) {
+      if (k_due) commit(0, PAR);
+      if (v_due) commit(1, 1 - PAR);
     }
-    // fp8: the tiles loaded above reach their buffers (free since this iteration's barrier)
-    // before the next iteration's barrier
-    if (j + 2 < ntiles) commit(0, PAR);
-    if (j + 1 < ntiles) commit(1, 1 - PAR);
+    if constexpr (FP8) {
+      // the codes the next iteration converts: K(j+3) and V(j+2)
+      if (j + 3 < ntiles) issue(j + 3, idK, 0, 0);
+      if (j + 2 < ntiles) issue(j + 2, idV, 1, 0);
+    }
   };
   for (int j = 0; j < ntiles; j += 2) {
     iteration(j, I0(), sa, sb);
