@@ -1,7 +1,8 @@
 """GPU parity on seeded random batches: the parameter space the fixed cases sample by hand
 (head dim, block size, GQA group, split sizes, query tile, verify rows, the mix of decode,
 draft and prefill rows), drawn jointly, each batch checked against the fp64 oracle at the same
-bars as the fixed cases. Every case prints its seed and shapes before it runs."""
+bars as the fixed cases (the unified launch over bf16 and over fp8 pages, and the decode
+entry). Every case prints its seed and shapes before it runs."""
 import numpy as np
 import pytest
 
@@ -54,3 +55,22 @@ def test_random_decode_batches(seed, dtype):
     w = synth.custom_workload(q, ctx, hkv * g, hkv, d, bs, dtype=dtype, seed=seed,
                               spare_blocks=int(rng.integers(0, 4)))
     small_case(w, "decode", dec_split=int(rng.choice([64, 256, 1024])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_mixed_batches_fp8(seed):
+    """Unified launch over fp8 pages, on the same random space as the bf16 batches."""
+    from tests.test_gpu_fp8_varlen import fp8_case
+    rng = np.random.default_rng(9000 + seed)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    q, ctx = _batch(rng, 10, decode_only=False)
+    tiling = dict(dec_split=int(rng.choice([64, 128, 512, 4096])),
+                  pf_q_tile=int(rng.choice([16, 64, 100, 128])),
+                  pf_kv_split=int(rng.choice([0, 64, 192, 512])),
+                  verify_rows=int(rng.choice([0, 4, 8])))
+    w = synth.custom_workload(q, ctx, hkv * g, hkv, d, bs, seed=seed,
+                              spare_blocks=int(rng.integers(0, 4)))
+    fp8_case(w, values_on="cpu", **tiling)
