@@ -1452,31 +1452,19 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
 // (bf16) -- set the page maximum, the new scale is the smallest power of two 2^k (k >= -120)
 // with max <= 448 * 2^k, and every valid row is encoded again as the round-to-nearest-even
 // E4M3FN code of value * 2^-k (an exact scaling). Rows past the context stay untouched.
-// Grid: x = packed token, y = groups of four (tensor, kv head) units, one wave per unit. Only
-// the token that is the first new row of its block does work, so each touched page is
-// rewritten by exactly one wave. Two passes over the page: the maximum, then the codes; each
-// lane reads and writes the same eight codes in both, and the new codes and scale depend on
-// the maximum over all lanes' reads, so no write precedes a read of the old page.
+// Grid: x = runs of `tokens_per_group` consecutive packed tokens, y = groups of four (tensor,
+// kv head) units, one wave per unit. A page is rewritten by the wave that meets the first new
+// row of its block, so each touched page is rewritten by exactly one wave; a wave walks its run
+// from one block's first row to the next, so runs of prefill tokens cost one step per page,
+// not per token. Two passes over the page: the maximum, then the codes; each lane reads and
+// writes the same eight codes in both, and the new codes and scale depend on the maximum over
+// all lanes' reads, so no write precedes a read of the old page.
 template <int D>
-__global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
-    const __bf16* k_new, const __bf16* v_new, uint8_t* k_pages, uint8_t* v_pages,
-    float* scales, const int32_t* block_table, int32_t max_blocks,
-    const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
-    int32_t num_kv_heads, int32_t block_size, int32_t bs_shift) {
-  const int unit = blockIdx.y * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (unit >= 2 * num_kv_heads) return;
-  const int t = blockIdx.x;
-  int lo_s = 0, hi_s = num_seqs;  // cu[lo_s] <= t < cu[hi_s]
-  while (hi_s - lo_s > 1) {
-    const int mid = (lo_s + hi_s) >> 1;
-    if (cu_seqlens[mid] <= t) lo_s = mid; else hi_s = mid;
-  }
-  const int s = lo_s;
-  const int qlen = cu_seqlens[s + 1] - cu_seqlens[s];
-  const int ctx = context_lens[s];
-  const int P = ctx - qlen;
-  const int pos = P + (t - cu_seqlens[s]);
-  if (pos != P && (pos & (block_size - 1)) != 0) return;  // not the first new row of its block
+__device__ void rewrite_fp8_page(const __bf16* k_new, const __bf16* v_new, uint8_t* k_pages,
+                                 uint8_t* v_pages, float* scales, const int32_t* block_table,
+                                 int32_t max_blocks, int32_t num_kv_heads, int32_t block_size,
+                                 int32_t bs_shift, int unit, int s, int c0, int ctx, int P,
+                                 int pos) {
   const int lb = pos >> bs_shift;
   const int row0 = lb << bs_shift;                          // position of the block's slot 0
   const int n_valid = min(ctx, row0 + block_size) - row0;
@@ -1489,7 +1477,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
                    (static_cast<size_t>(blk) * num_kv_heads + g) * block_size * D;
   float* scale_p = scales + 2 * (static_cast<size_t>(blk) * num_kv_heads + g) + which;
   const __bf16* src = (which ? v_new : k_new) + g * D;
-  const int64_t tok_p = static_cast<int64_t>(cu_seqlens[s]) - P;  // packed token of position 0
+  const int64_t tok_p = static_cast<int64_t>(c0) - P;     // packed token of position 0
   const float old_scale = n_old > 0 ? *scale_p : 1.f;
   constexpr int Q8 = D / 8;                                 // eight-code groups per row
   const int groups = n_valid * Q8;
@@ -1548,6 +1536,41 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
     *reinterpret_cast<u32x2*>(codes + j * D + 8 * q) = w;
   }
   if (lane == 0) *scale_p = ldexpf(1.f, k);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
+    const __bf16* k_new, const __bf16* v_new, uint8_t* k_pages, uint8_t* v_pages,
+    float* scales, const int32_t* block_table, int32_t max_blocks,
+    const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_tokens, int32_t tokens_per_group, int32_t num_kv_heads, int32_t block_size,
+    int32_t bs_shift) {
+  const int unit = blockIdx.y * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= 2 * num_kv_heads) return;
+  const int t0 = blockIdx.x * tokens_per_group;
+  const int t1 = min(t0 + tokens_per_group, num_tokens);
+  int lo_s = 0, hi_s = num_seqs;  // cu[lo_s] <= t0 < cu[hi_s]
+  while (hi_s - lo_s > 1) {
+    const int mid = (lo_s + hi_s) >> 1;
+    if (cu_seqlens[mid] <= t0) lo_s = mid; else hi_s = mid;
+  }
+  int s = lo_s;
+  for (int t = t0; t < t1 && s < num_seqs;) {
+    const int c0 = cu_seqlens[s], c1 = cu_seqlens[s + 1];
+    if (t >= c1) {
+      ++s;
+      continue;
+    }
+    const int ctx = context_lens[s];
+    const int P = ctx - (c1 - c0);
+    const int pos = P + (t - c0);
+    // the first new row of its block: this wave rewrites the page
+    if (pos == P || (pos & (block_size - 1)) == 0)
+      rewrite_fp8_page<D>(k_new, v_new, k_pages, v_pages, scales, block_table, max_blocks,
+                          num_kv_heads, block_size, bs_shift, unit, s, c0, ctx, P, pos);
+    // the next block's first row, or the next sequence's first token
+    t = min(t + ((pos | (block_size - 1)) + 1) - pos, c1);
+  }
 }
 
 int log2i(int x) {
@@ -1918,12 +1941,17 @@ extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void*
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int shift = log2i(block_size);
   const unsigned units = (2 * num_kv_heads + kThreads / 64 - 1) / (kThreads / 64);
+  // runs of tokens per workgroup: one token each up to kFp8WriteRuns tokens (decode batches:
+  // every token starts its page), longer runs beyond (prefill chunks: one page per block)
+  constexpr int kFp8WriteRuns = 4096;
+  const int per_group = (num_tokens + kFp8WriteRuns - 1) / kFp8WriteRuns;
+  const int groups = (num_tokens + per_group - 1) / per_group;
 #define PA_RC8_LAUNCH(DD)                                                                      \
-  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DD>, dim3(num_tokens, units), dim3(kThreads), 0, st, \
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DD>, dim3(groups, units), dim3(kThreads), 0, st, \
                      static_cast<const __bf16*>(k_new), static_cast<const __bf16*>(v_new),      \
                      static_cast<uint8_t*>(k_pages), static_cast<uint8_t*>(v_pages), scales,    \
                      block_table, max_blocks_per_seq, cu_seqlens_q, context_lens,               \
-                     num_seqs, num_kv_heads, block_size, shift)
+                     num_seqs, num_tokens, per_group, num_kv_heads, block_size, shift)
   if (head_dim == 128)
     PA_RC8_LAUNCH(128);
   else
