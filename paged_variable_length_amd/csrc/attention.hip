@@ -114,6 +114,21 @@ struct DecodeVRaw<64> {
   typedef u32x2 type;  // 4 bf16 along D
 };
 
+// Float index of (row, d) in the merge buffer sm_acc ([4 waves x 16 columns] rows of D). Each
+// lane stores its column's d = VEC*(4*g4 + r) + n for fixed (r, n) in one instruction, so
+// unpadded rows (D floats, a multiple of the bank count) would put the 16 columns of a lane
+// group in one bank. Rows of D + 1 floats spread them: at D = 64 the 64 lanes of a store hit
+// 64 distinct banks; at D = 128, lanes g4 and g4 + 2 of one column (64 floats apart) still share
+// a bank, a two-way conflict where there were sixteen. The merge's reads (consecutive d of one
+// row) stay contiguous.
+template <int D>
+__device__ __forceinline__ int merge_idx(int row, int d) {
+  return row * (D + 1) + d;
+}
+// floats of the decode merge buffers: sm_m, sm_l [4][16] each, sm_acc [64 padded rows]
+template <int D>
+constexpr int kMergeFloats = 128 + 64 * (D + 1);
+
 // Merge of the four waves' partial states per score column, then the output row or an fp32
 // partial. Column c is (row c / G, head c % G); rows are relative to packed row tok.
 template <int D>
@@ -128,7 +143,7 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
   l += wave_shfl_xor(l, 32);
   float* sm_m = smem;              // [4][16]
   float* sm_l = smem + 64;         // [4][16]
-  float* sm_acc = smem + 128;      // [4][16][D]
+  float* sm_acc = smem + 128;      // [4][16] padded rows of D (merge_idx)
   if (g4 == 0) {
     sm_m[wave * 16 + i16] = m;
     sm_l[wave * 16 + i16] = l;
@@ -137,7 +152,8 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
 #pragma unroll
     for (int n = 0; n < VEC; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_acc[(wave * 16 + i16) * D + VEC * (4 * g4 + r) + n] = acc[n][r];
+      for (int r = 0; r < 4; ++r)
+        sm_acc[merge_idx<D>(wave * 16 + i16, VEC * (4 * g4 + r) + n)] = acc[n][r];
   }
   __syncthreads();
   const int hq0 = t.head * G;
@@ -153,7 +169,7 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
     for (int w = 0; w < 4; ++w) {
       const float wt = fast_exp2(sm_m[w * 16 + h] - Muse);
       L += wt * sm_l[w * 16 + h];
-      A += wt * sm_acc[(w * 16 + h) * D + d];
+      A += wt * sm_acc[merge_idx<D>(w * 16 + h, d)];
     }
     if (t.partial < 0) {
       const int row = h / G, hh = h - row * G;
@@ -1331,7 +1347,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
-  __shared__ float smem[128 + 4 * 16 * D];
+  __shared__ float smem[kMergeFloats<D>];
   const pa_task t = a.tasks[blockIdx.x];
   if (t.kind != PA_TASK_DECODE && t.kind != PA_TASK_SHARED) return;
   if constexpr (sizeof(T) == 2)
@@ -1342,7 +1358,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
-  __shared__ float smem[128 + 4 * 16 * D];
+  __shared__ float smem[kMergeFloats<D>];
   const pa_task t = a.tasks[blockIdx.x];
   // verify tasks need the packed rows' offsets (cu_seqlens), which only the verify entry passes;
   // shared-prefix tasks address their members' rows as consecutive decode rows (no cu_seqlens)
@@ -1355,7 +1371,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
-  constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
+  constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
   __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_PREFILL)
@@ -1368,7 +1384,7 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
-  constexpr size_t kDecode = (128 + 4 * 16 * D) * sizeof(float);
+  constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
   __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_PREFILL)
