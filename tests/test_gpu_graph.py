@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["decode_mha_bf16", "verify_gqa_fp8", "prefill_varlen_bf16",
-                                  "decode_shared_mha_bf16"])
+                                  "decode_shared_mha_bf16", "mixed_fp8"])
 def test_graph_replays_match_eager_step(name):
     print(f"\n[case] graph replay {name}", flush=True)
     r = bench.Runner(name)
