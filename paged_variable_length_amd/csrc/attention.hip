@@ -884,6 +884,13 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   auto dma_off = [&](int i) -> uint32_t {
     return dma0 ^ ((lds_swz<D>(key0 + i * C::kKeysPerLoad) ^ lds_swz<D>(key0)) << 4);
   };
+  // The pieces' lane offsets within a tile, dma_off(i) + 1024*i, computed once and held across
+  // the loop (P registers): each direct load of a full tile then takes the tile's block address
+  // as a scalar base and its own never-rewritten offset register. Addresses rebuilt before
+  // every load in one register pair make each load wait until the previous one has read it.
+  uint32_t dmo[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) dmo[i] = dma_off(i) + i * 1024;
   const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
   // block id of this wave's keys in tile `tile`; keys past the range are clamped, so any tile
   // number is safe
@@ -909,25 +916,27 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       for (int i = 0; i < P; ++i) {
         uint32_t off;
         if (full) {
-          off = tile_slot + dma_off(i) + i * 1024;
+          off = tile_slot + dmo[i];
         } else {
           const int kabs = min(ts + key0 + i * C::kKeysPerLoad, kv1 - 1);
-          off = (kabs & (bs - 1)) * C::kRowBytes + (dma_off(i) & (C::kRowBytes - 1));
+          off = (kabs & (bs - 1)) * C::kRowBytes + (dmo[i] & (C::kRowBytes - 1));
         }
         stage[which][i] = *reinterpret_cast<const u32x2*>(page + off / 2);
       }
     } else if (full) {
+      const char* base = page + tile_slot;
 #pragma unroll
       for (int i = 0; i < P; ++i)
-        __builtin_amdgcn_global_load_lds(page + tile_slot + dma_off(i) + i * 1024,
+        __builtin_amdgcn_global_load_lds(base + dmo[i],
                                          (__attribute__((address_space(3))) void*)(dst0 + i * 1024),
                                          16, 0, 0);
+      asm volatile("");  // keeps this path's last load from being merged with the partial path's
     } else {
 #pragma unroll
       for (int i = 0; i < P; ++i) {
         const int kabs = min(ts + key0 + i * C::kKeysPerLoad, kv1 - 1);
         __builtin_amdgcn_global_load_lds(
-            page + (kabs & (bs - 1)) * C::kRowBytes + (dma_off(i) & (C::kRowBytes - 1)),
+            page + (kabs & (bs - 1)) * C::kRowBytes + (dmo[i] & (C::kRowBytes - 1)),
             (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16, 0, 0);
       }
     }
@@ -1246,7 +1255,11 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     constexpr int PAR = decltype(par_tag)::value;
     // opaque redefinition: values derived from these bases (the per-k-step and per-piece
     // addresses) are then recomputed where used instead of held in registers across the loop
-    asm volatile("" : "+v"(ka0), "+v"(dma0));
+    asm volatile("" : "+v"(ka0));
+    // the offsets stay 32-bit values in their own registers, so each load can take them as its
+    // offset operand next to the scalar base
+#pragma unroll
+    for (int i = 0; i < P; ++i) asm volatile("" : "+v"(dmo[i]));
     if (j > 0 || ntiles > 2) {
       if constexpr (FP8) {
         lds_barrier();
