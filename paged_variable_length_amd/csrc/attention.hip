@@ -884,13 +884,14 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   auto dma_off = [&](int i) -> uint32_t {
     return dma0 ^ ((lds_swz<D>(key0 + i * C::kKeysPerLoad) ^ lds_swz<D>(key0)) << 4);
   };
-  // The pieces' lane offsets within a tile, dma_off(i) + 1024*i, computed once and held across
-  // the loop (P registers): each direct load of a full tile then takes the tile's block address
-  // as a scalar base and its own never-rewritten offset register. Addresses rebuilt before
-  // every load in one register pair make each load wait until the previous one has read it.
+  // The pieces' lane offsets within a tile, dma_off(i) + 1024*i (fp8: half of it, the offset of
+  // the same elements' codes), computed once and held across the loop (P registers): each load
+  // of a full tile then takes the tile's block address as a scalar base and its own
+  // never-rewritten offset register. Addresses rebuilt before every load in one register make
+  // each load wait until the previous one has read it.
   uint32_t dmo[P];
 #pragma unroll
-  for (int i = 0; i < P; ++i) dmo[i] = dma_off(i) + i * 1024;
+  for (int i = 0; i < P; ++i) dmo[i] = FP8 ? (dma_off(i) + i * 1024) / 2 : dma_off(i) + i * 1024;
   const int ntiles = (kv1 - kv0 + C::kTile - 1) / C::kTile;
   // block id of this wave's keys in tile `tile`; keys past the range are clamped, so any tile
   // number is safe
@@ -912,16 +913,18 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     const uint32_t tile_slot = static_cast<uint32_t>(ts & (bs - 1)) * C::kRowBytes;
     if constexpr (FP8) {
       stage_sc[which] = ((cfloat*)a.scales)[2 * (static_cast<size_t>(id) * a.num_kv_heads + kvh) + which];
+      if (full) {
+        const char* base = page + tile_slot / 2;
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        uint32_t off;
-        if (full) {
-          off = tile_slot + dmo[i];
-        } else {
+        for (int i = 0; i < P; ++i) stage[which][i] = *reinterpret_cast<const u32x2*>(base + dmo[i]);
+        asm volatile("");
+      } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
           const int kabs = min(ts + key0 + i * C::kKeysPerLoad, kv1 - 1);
-          off = (kabs & (bs - 1)) * C::kRowBytes + (dmo[i] & (C::kRowBytes - 1));
+          stage[which][i] = *reinterpret_cast<const u32x2*>(
+              page + (kabs & (bs - 1)) * (C::kRowBytes / 2) + (dmo[i] & (C::kRowBytes / 2 - 1)));
         }
-        stage[which][i] = *reinterpret_cast<const u32x2*>(page + off / 2);
       }
     } else if (full) {
       const char* base = page + tile_slot;
