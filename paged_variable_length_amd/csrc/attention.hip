@@ -41,6 +41,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// read-only data reached through the constant address space, so uniform indexes load it
+// with scalar loads
+typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(4))) const float cfloat;
 
 constexpr int kThreads = 256;  // 4 waves of 64
 constexpr float kLog2e = 1.4426950408889634f;
@@ -198,7 +202,9 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
   constexpr int KS = D / 32;
   constexpr int VEC = D / 16;
   typedef typename DecodeVRaw<D>::type VRaw;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: chunk indices, tile bounds and block ids stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, g4 = lane >> 4;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int s = t.seq, kvh = t.head;
@@ -233,7 +239,7 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pages) + kvh * head_stride;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pages) + kvh * head_stride;
-  const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_blocks;
+  cint32* bt = (cint32*)(a.block_table + static_cast<size_t>(s) * a.max_blocks);
   const float c = a.scale_log2;
 
   f32x4 acc[VEC];
@@ -243,36 +249,35 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
 
   const int kv0 = t.kv0, kv1 = t.kv1;
   const int nchunks = (kv1 - kv0 + 31) >> 5;
+  // block ids of a chunk's two 16-key tiles, by scalar loads one chunk ahead of their use. A
+  // tile past kv1 takes the block of key kv1 - 1: its loads read rows of a valid page, and the
+  // tail masking below gives them no weight.
+  auto chunk_blocks = [&](int ch, int (&blk)[2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) blk[tt] = bt[min(kv0 + 32 * ch + 16 * tt, kv1 - 1) >> a.bs_shift];
+  };
+  int blk[2];
+  chunk_blocks(wave, blk);
   for (int ch = wave; ch < nchunks; ch += 4) {
     const int cs = kv0 + 32 * ch;
     size_t off[2];
-    bool tv[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int ts = cs + 16 * tt;
-      tv[tt] = ts < kv1;
-      const int blk = tv[tt] ? bt[ts >> a.bs_shift] : 0;
-      off[tt] = static_cast<size_t>(blk) * block_stride + static_cast<size_t>(ts & (bs - 1)) * D;
-    }
+    for (int tt = 0; tt < 2; ++tt)
+      off[tt] = static_cast<size_t>(blk[tt]) * block_stride +
+                static_cast<size_t>((cs + 16 * tt) & (bs - 1)) * D;
+    chunk_blocks(ch + 4, blk);
     bf16x8 kf[2][KS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (tv[tt])
-          v = *reinterpret_cast<const u32x4*>(kbase + off[tt] + i16 * D + 32 * ks + 8 * g4);
-        kf[tt][ks] = as_bf16x8(v);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kf[tt][ks] = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(kbase + off[tt] + i16 * D + 32 * ks + 8 * g4));
     VRaw vr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tt = e >> 2;
-      VRaw v = {};
-      if (tv[tt])
-        v = *reinterpret_cast<const VRaw*>(vbase + off[tt] + (4 * g4 + (e & 3)) * D + VEC * i16);
-      vr[e] = v;
-    }
+    for (int e = 0; e < 8; ++e)
+      vr[e] = *reinterpret_cast<const VRaw*>(vbase + off[e >> 2] + (4 * g4 + (e & 3)) * D +
+                                             VEC * i16);
     f32x4 sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -282,8 +287,9 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
         sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[ks], sc[tt], 0, 0, 0);
     }
     if (cs + 32 > kv1) {
-      // tail chunk: keys past kv1 get no weight, and their (possibly non-finite) values are
-      // replaced by zeros so that 0 * value stays 0 in the value product
+      // tail chunk: keys past kv1 get no weight, and the values loaded for them (rows of some
+      // valid page, possibly non-finite) are replaced by zeros so that 0 * value stays 0 in the
+      // value product
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = cs + 16 * (e >> 2) + 4 * g4 + (e & 3);
@@ -770,9 +776,6 @@ __device__ __forceinline__ void lds_wait(T (&r)[4]) {
                : "n"(K)
                : "memory");
 }
-
-typedef __attribute__((address_space(4))) const int32_t cint32;
-typedef __attribute__((address_space(4))) const float cfloat;
 
 // Causal mask of one 32-key block of S^T scores: register r holds key offset
 // BASE + 8*(r/4) + r%4 (plus the lane's own offset, folded into lim); offsets >= lim become
