@@ -197,7 +197,7 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
   }
 }
 
-template <int D>
+template <int D, bool AHEAD>
 __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* smem) {
   constexpr int KS = D / 32;
   constexpr int VEC = D / 16;
@@ -256,28 +256,26 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) blk[tt] = bt[min(kv0 + 32 * ch + 16 * tt, kv1 - 1) >> a.bs_shift];
   };
-  int blk[2];
-  chunk_blocks(wave, blk);
-  for (int ch = wave; ch < nchunks; ch += 4) {
+  auto load_chunk = [&](int ch, const int (&blk)[2], bf16x8 (&kf)[2][KS], VRaw (&vr)[8]) {
     const int cs = kv0 + 32 * ch;
     size_t off[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
       off[tt] = static_cast<size_t>(blk[tt]) * block_stride +
                 static_cast<size_t>((cs + 16 * tt) & (bs - 1)) * D;
-    chunk_blocks(ch + 4, blk);
-    bf16x8 kf[2][KS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         kf[tt][ks] = as_bf16x8(
             *reinterpret_cast<const u32x4*>(kbase + off[tt] + i16 * D + 32 * ks + 8 * g4));
-    VRaw vr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vr[e] = *reinterpret_cast<const VRaw*>(vbase + off[e >> 2] + (4 * g4 + (e & 3)) * D +
                                              VEC * i16);
+  };
+  auto compute_chunk = [&](int ch, const bf16x8 (&kf)[2][KS], VRaw (&vr)[8]) {
+    const int cs = kv0 + 32 * ch;
     f32x4 sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -336,6 +334,34 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
       for (int qd = 0; qd < 4; ++qd)
         vw[qd] = pair_half(vr[2 * qd][n >> 1], vr[2 * qd + 1][n >> 1], n & 1);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+    }
+  };
+  // A wave takes chunks wave, wave + 4, ...; with AHEAD it issues the loads of its next chunk
+  // before it computes the current one (two register sets, taken in turn), so two chunks of
+  // loads are in flight per wave.
+  int blk[2];
+  chunk_blocks(wave, blk);
+  if constexpr (AHEAD) {
+    bf16x8 ka[2][KS], kb[2][KS];
+    VRaw va[8], vb[8];
+    if (wave < nchunks) load_chunk(wave, blk, ka, va);
+    chunk_blocks(wave + 4, blk);
+    for (int ch = wave; ch < nchunks; ch += 8) {
+      if (ch + 4 < nchunks) load_chunk(ch + 4, blk, kb, vb);
+      chunk_blocks(ch + 8, blk);
+      compute_chunk(ch, ka, va);
+      if (ch + 4 >= nchunks) break;
+      if (ch + 8 < nchunks) load_chunk(ch + 8, blk, ka, va);
+      chunk_blocks(ch + 12, blk);
+      compute_chunk(ch + 4, kb, vb);
+    }
+  } else {
+    for (int ch = wave; ch < nchunks; ch += 4) {
+      bf16x8 kf[2][KS];
+      VRaw vr[8];
+      load_chunk(ch, blk, kf, vr);
+      chunk_blocks(ch + 4, blk);
+      compute_chunk(ch, kf, vr);
     }
   }
   decode_merge_and_store<D>(a, t, tok, G, ncol, m, l, acc, smem, true);
@@ -1365,12 +1391,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void decode_kernel(AttnArgs a) {
   __shared__ float smem[kMergeFloats<D>];
   const pa_task t = a.tasks[blockIdx.x];
   if (t.kind != PA_TASK_DECODE && t.kind != PA_TASK_SHARED) return;
   if constexpr (sizeof(T) == 2)
-    decode_task_bf16<D>(a, t, smem);
+    decode_task_bf16<D, false>(a, t, smem);
   else
     decode_task_f32<D>(a, t, smem);
 }
@@ -1396,7 +1422,7 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   if (t.kind == PA_TASK_PREFILL)
     prefill_task<D>(a, t, smem);
   else
-    decode_task_bf16<D>(a, t, reinterpret_cast<float*>(smem));
+    decode_task_bf16<D, true>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // The unified launch over fp8 pages: every task kind, rows addressed through cu_seqlens.
