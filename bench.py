@@ -45,11 +45,13 @@ SECONDARY = ["decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64", "prefill_varlen_bf1
              "decode_shared_mha_bf16", "decode_shared_mha_bf16:no_sharing",
              "gemm_linear_prefill_qproj", "gemm_linear_mixed_oproj", "gemm_linear_1024x1024x1024",
              "gemm_linear_512x2048x1024", "gemm_linear_2048x512x2048"]
-# Split sizes per workload, from a sweep on MI355X (decode: 512 .. 8192 keys; mixed: key
+# Split sizes per workload, from a sweep on MI355X (decode: 512 .. 32768 keys; mixed: key
 # splits of 4096 .. 32768 and none for prefill tiles). Larger decode splits amortise each task's
-# query load, four-wave merge and partial write; the load-sorted table keeps the tail short.
+# query load, four-wave merge and partial write; the load-sorted table keeps the tail short. The
+# MHA batches (contexts up to 4096) run unsplit: one task per sequence and head, writing `out`
+# directly, with no partial rows and no combine.
 TILING = {
-    "decode_mha_bf16": dict(dec_split=1024),
+    "decode_mha_bf16": dict(dec_split=4096),
     "decode_gqa_bf16_bs16": dict(dec_split=8192),
     "decode_gqa_bf16_bs64": dict(dec_split=8192),
     "prefill_varlen_bf16": dict(pf_q_tile=128, pf_kv_split=0),
@@ -60,8 +62,8 @@ TILING = {
     "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
     # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline), and the
     # verify batch over fp8 pages
-    "decode_mha_fp8": dict(dec_split=1024),
-    "verify_gqa_fp8": dict(dec_split=8192, verify_rows=4),
+    "decode_mha_fp8": dict(dec_split=4096),
+    "verify_gqa_fp8": dict(dec_split=32768, verify_rows=4),
     # the prefill batch and the mixed step over fp8 pages, through the unified fp8 launch
     "prefill_varlen_fp8": dict(pf_q_tile=128, pf_kv_split=0),
     "mixed_fp8": dict(dec_split=4096, pf_q_tile=128, pf_kv_split=0),

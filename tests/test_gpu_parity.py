@@ -171,9 +171,10 @@ def test_single_key_returns_value_exactly_on_gpu():
 
 @pytest.mark.parametrize("name", ["decode_mha_bf16", "decode_gqa_bf16_bs16", "decode_gqa_bf16_bs64"])
 def test_decode_full_size(name):
-    """Full-size decode workloads in the launch configuration bench.py times (its TILING: key
-    splits of 1024 for the MHA batch, 8192 for the GQA batches); the oracle checks a seeded
-    sample of sequences that always holds the shortest and the longest."""
+    """Full-size decode workloads in the launch configuration bench.py times (its TILING: the
+    MHA batch unsplit, one task per sequence and head writing `out` directly; key splits of 8192
+    merged by the combine for the GQA batches); the oracle checks a seeded sample of sequences
+    that always holds the shortest and the longest."""
     w = synth.make_workload(name)
     _announce(f"decode full {name} N={w.num_seqs}")
     rng = np.random.default_rng(0)
