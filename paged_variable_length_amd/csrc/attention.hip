@@ -197,7 +197,17 @@ __device__ __forceinline__ void decode_merge_and_store(const AttnArgs& a, const 
   }
 }
 
-template <int D, bool AHEAD>
+// A page read; NT marks it non-temporal (the line is a first candidate for eviction), for page
+// streams that are read once per launch and should not push reused lines out of the caches.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <int D, bool AHEAD, bool NT>
 __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* smem) {
   constexpr int KS = D / 32;
   constexpr int VEC = D / 16;
@@ -267,12 +277,12 @@ __device__ void decode_task_bf16(const AttnArgs& a, const pa_task& t, float* sme
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kf[tt][ks] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(kbase + off[tt] + i16 * D + 32 * ks + 8 * g4));
+        kf[tt][ks] = as_bf16x8(ld<NT>(
+            reinterpret_cast<const u32x4*>(kbase + off[tt] + i16 * D + 32 * ks + 8 * g4)));
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      vr[e] = *reinterpret_cast<const VRaw*>(vbase + off[e >> 2] + (4 * g4 + (e & 3)) * D +
-                                             VEC * i16);
+      vr[e] = ld<NT>(reinterpret_cast<const VRaw*>(
+          vbase + off[e >> 2] + (4 * g4 + (e & 3)) * D + VEC * i16));
   };
   auto compute_chunk = [&](int ch, const bf16x8 (&kf)[2][KS], VRaw (&vr)[8]) {
     const int cs = kv0 + 32 * ch;
@@ -408,7 +418,7 @@ __device__ __forceinline__ uint32_t vslot_word(const typename Fp8VRaw<D>::type& 
     return v;
 }
 
-template <int D>
+template <int D, bool NT>
 __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem) {
   constexpr int KS = D / 32;
   constexpr int KJ = D / 64;
@@ -464,10 +474,11 @@ __device__ void decode_task_fp8(const AttnArgs& a, const pa_task& t, float* smem
           static_cast<size_t>(blk[tt]) * block_stride + static_cast<size_t>(ts & (bs - 1)) * D;
 #pragma unroll
       for (int j = 0; j < KJ; ++j)
-        r.k[tt][j] = *reinterpret_cast<const u32x4*>(kbase + off + i16 * D + 64 * j + 16 * g4);
+        r.k[tt][j] = ld<NT>(reinterpret_cast<const u32x4*>(kbase + off + i16 * D + 64 * j + 16 * g4));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        r.v[4 * tt + e] = *reinterpret_cast<const VRaw*>(vbase + off + (4 * g4 + e) * D + VEC * i16);
+        r.v[4 * tt + e] =
+            ld<NT>(reinterpret_cast<const VRaw*>(vbase + off + (4 * g4 + e) * D + VEC * i16));
       // the K and V scales of a page sit side by side: one 8-byte read
       const size_t page = static_cast<size_t>(blk[tt]) * a.num_kv_heads + kvh;
       const f32x2 sc = *reinterpret_cast<const f32x2*>(a.scales + 2 * page);
@@ -1396,7 +1407,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(AttnArgs a) {
   const pa_task t = a.tasks[blockIdx.x];
   if (t.kind != PA_TASK_DECODE && t.kind != PA_TASK_SHARED) return;
   if constexpr (sizeof(T) == 2)
-    decode_task_bf16<D, false>(a, t, smem);
+    decode_task_bf16<D, false, true>(a, t, smem);
   else
     decode_task_f32<D>(a, t, smem);
 }
@@ -1410,10 +1421,12 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
   if (t.kind == PA_TASK_PREFILL || (t.kind == PA_TASK_VERIFY && !a.cu_seqlens) ||
       (t.kind == PA_TASK_SHARED && a.cu_seqlens))
     return;
-  decode_task_fp8<D>(a, t, smem);
+  decode_task_fp8<D, true>(a, t, smem);
 }
 
-template <int D>
+// NT: the table holds no prefill tiles, so the decode tasks' page streams have nothing reused in
+// the caches to protect (non-temporal reads measured faster there, and slower beside prefill tiles)
+template <int D, bool NT>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
@@ -1422,11 +1435,11 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   if (t.kind == PA_TASK_PREFILL)
     prefill_task<D>(a, t, smem);
   else
-    decode_task_bf16<D, true>(a, t, reinterpret_cast<float*>(smem));
+    decode_task_bf16<D, true, NT>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // The unified launch over fp8 pages: every task kind, rows addressed through cu_seqlens.
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
@@ -1435,7 +1448,7 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) 
   if (t.kind == PA_TASK_PREFILL)
     prefill_task<D, true>(a, t, smem);
   else
-    decode_task_fp8<D>(a, t, reinterpret_cast<float*>(smem));
+    decode_task_fp8<D, NT>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // One workgroup per combine record; each wave merges one (row, head) at a time.
@@ -1857,25 +1870,31 @@ int varlen_enqueue(const char* who, const void* q, const void* k_pages, const vo
                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, float scale, const pa_task* tasks_dev, int32_t num_tasks,
                    const pa_combine* combines_dev, int32_t num_combines, int32_t num_partials,
-                   void* workspace, void* out, void* stream, const float* scales = nullptr) {
+                   uint32_t task_kinds, void* workspace, void* out, void* stream,
+                   const float* scales = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool nt = !(task_kinds & PA_KIND_BIT(PA_TASK_PREFILL));
   AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                          context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                          tasks_dev, num_tasks, num_partials, workspace, out);
   a.scales = scales;  // fp8 pages when set
+  void (*kernel)(AttnArgs);
   if (head_dim == 128) {
     if (scales)
-      hipLaunchKernelGGL(meta_attn_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+      kernel = nt ? meta_attn_fp8_kernel<128, true> : meta_attn_fp8_kernel<128, false>;
     else
-      hipLaunchKernelGGL(meta_attn_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
-    launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
+      kernel = nt ? meta_attn_kernel<128, true> : meta_attn_kernel<128, false>;
   } else {
     if (scales)
-      hipLaunchKernelGGL(meta_attn_fp8_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+      kernel = nt ? meta_attn_fp8_kernel<64, true> : meta_attn_fp8_kernel<64, false>;
     else
-      hipLaunchKernelGGL(meta_attn_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
-    launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
+      kernel = nt ? meta_attn_kernel<64, true> : meta_attn_kernel<64, false>;
   }
+  hipLaunchKernelGGL(kernel, dim3(num_tasks), dim3(kThreads), 0, st, a);
+  if (head_dim == 128)
+    launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
+  else
+    launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
   return hip_check(who);
 }
 
@@ -1902,7 +1921,7 @@ extern "C" int paged_attn_varlen_prefill(
   return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                         tasks_dev, num_tasks, combines_dev, num_combines, num_partials,
-                        workspace, out, stream);
+                        task_kinds, workspace, out, stream);
 }
 
 // Partial rows of paged_attn_varlen_prefill_noalloc: device memory the library holds itself.
@@ -1971,8 +1990,8 @@ extern "C" int paged_attn_varlen_prefill_noalloc(
     if (int rc = scratch_of_current_device(who, &ws)) return rc;
   return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
-                        tasks_dev, num_tasks, combines_dev, num_combines, num_partials, ws, out,
-                        stream);
+                        tasks_dev, num_tasks, combines_dev, num_combines, num_partials,
+                        task_kinds, ws, out, stream);
 }
 
 extern "C" int reshape_and_cache_fp8(const void* k_new, const void* v_new, void* k_pages,
@@ -2118,5 +2137,5 @@ extern "C" int paged_attn_varlen_prefill_fp8(
   return varlen_enqueue(who, q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                         context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                         tasks_dev, num_tasks, combines_dev, num_combines, num_partials,
-                        workspace, out, stream, scales);
+                        task_kinds, workspace, out, stream, scales);
 }
