@@ -68,6 +68,7 @@ struct AttnArgs {
   int32_t bs_shift;
   int32_t num_tasks;
   float scale_log2;             // softmax scale * log2(e)
+  int32_t stream_reads;         // unified launch: decode page reads non-temporal (no prefill tiles)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -1424,9 +1425,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_kernel(AttnArgs a) {
   decode_task_fp8<D, true>(a, t, smem);
 }
 
-// NT: the table holds no prefill tiles, so the decode tasks' page streams have nothing reused in
-// the caches to protect (non-temporal reads measured faster there, and slower beside prefill tiles)
-template <int D, bool NT>
+// a.stream_reads: the table holds no prefill tiles, so the decode tasks' page streams have nothing
+// reused in the caches to protect (non-temporal reads measured faster there, and slower beside
+// prefill tiles)
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
@@ -1434,12 +1436,14 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_PREFILL)
     prefill_task<D>(a, t, smem);
+  else if (a.stream_reads)
+    decode_task_bf16<D, true, true>(a, t, reinterpret_cast<float*>(smem));
   else
-    decode_task_bf16<D, true, NT>(a, t, reinterpret_cast<float*>(smem));
+    decode_task_bf16<D, true, false>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // The unified launch over fp8 pages: every task kind, rows addressed through cu_seqlens.
-template <int D, bool NT>
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) {
   constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
   constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
@@ -1447,8 +1451,10 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) 
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_PREFILL)
     prefill_task<D, true>(a, t, smem);
+  else if (a.stream_reads)
+    decode_task_fp8<D, true>(a, t, reinterpret_cast<float*>(smem));
   else
-    decode_task_fp8<D, NT>(a, t, reinterpret_cast<float*>(smem));
+    decode_task_fp8<D, false>(a, t, reinterpret_cast<float*>(smem));
 }
 
 // One workgroup per combine record; each wave merges one (row, head) at a time.
@@ -1741,6 +1747,7 @@ AttnArgs make_args(const void* q, const void* kp, const void* vp, const int32_t*
   a.bs_shift = log2i(bs);
   a.num_tasks = num_tasks;
   a.scale_log2 = scale * kLog2e;
+  a.stream_reads = 0;
   return a;
 }
 
@@ -1873,28 +1880,24 @@ int varlen_enqueue(const char* who, const void* q, const void* k_pages, const vo
                    uint32_t task_kinds, void* workspace, void* out, void* stream,
                    const float* scales = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool nt = !(task_kinds & PA_KIND_BIT(PA_TASK_PREFILL));
   AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, cu_seqlens_q,
                          context_lens, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                          tasks_dev, num_tasks, num_partials, workspace, out);
   a.scales = scales;  // fp8 pages when set
-  void (*kernel)(AttnArgs);
+  a.stream_reads = !(task_kinds & PA_KIND_BIT(PA_TASK_PREFILL));
   if (head_dim == 128) {
     if (scales)
-      kernel = nt ? meta_attn_fp8_kernel<128, true> : meta_attn_fp8_kernel<128, false>;
+      hipLaunchKernelGGL(meta_attn_fp8_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     else
-      kernel = nt ? meta_attn_kernel<128, true> : meta_attn_kernel<128, false>;
+      hipLaunchKernelGGL(meta_attn_kernel<128>, dim3(num_tasks), dim3(kThreads), 0, st, a);
+    launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
   } else {
     if (scales)
-      kernel = nt ? meta_attn_fp8_kernel<64, true> : meta_attn_fp8_kernel<64, false>;
+      hipLaunchKernelGGL(meta_attn_fp8_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     else
-      kernel = nt ? meta_attn_kernel<64, true> : meta_attn_kernel<64, false>;
-  }
-  hipLaunchKernelGGL(kernel, dim3(num_tasks), dim3(kThreads), 0, st, a);
-  if (head_dim == 128)
-    launch_combine<__bf16, 128>(combines_dev, num_combines, cu_seqlens_q, a, st);
-  else
+      hipLaunchKernelGGL(meta_attn_kernel<64>, dim3(num_tasks), dim3(kThreads), 0, st, a);
     launch_combine<__bf16, 64>(combines_dev, num_combines, cu_seqlens_q, a, st);
+  }
   return hip_check(who);
 }
 
