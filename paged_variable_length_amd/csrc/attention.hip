@@ -1402,13 +1402,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return base + (r & 7) * 8 + (r >> 3);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 3) void decode_kernel(AttnArgs a) {
+// AHEAD: each wave keeps two chunks of page reads in flight (two waves per SIMD) instead of one
+// (three waves per SIMD); measured faster on decode tables, slower on shared-prefix ones.
+template <typename T, int D, bool AHEAD>
+__global__ __launch_bounds__(kThreads, AHEAD ? 2 : 3) void decode_kernel(AttnArgs a) {
   __shared__ float smem[kMergeFloats<D>];
   const pa_task t = a.tasks[blockIdx.x];
   if (t.kind != PA_TASK_DECODE && t.kind != PA_TASK_SHARED) return;
   if constexpr (sizeof(T) == 2)
-    decode_task_bf16<D, false, true>(a, t, smem);
+    decode_task_bf16<D, AHEAD, true>(a, t, smem);
   else
     decode_task_f32<D>(a, t, smem);
 }
@@ -1823,20 +1825,28 @@ extern "C" int paged_attn_decode(const void* q, const void* k_pages, const void*
   const AttnArgs a = make_args(q, k_pages, v_pages, block_table, max_blocks_per_seq, nullptr,
                                context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
                                scale, tasks_dev, num_tasks, num_partials, workspace, out);
+  const bool ahead = !(task_kinds & PA_KIND_BIT(PA_TASK_SHARED));
+  const dim3 grid(num_tasks), block(kThreads);
   if (dtype == PA_BF16) {
     if (head_dim == 128) {
-      hipLaunchKernelGGL((decode_kernel<__bf16, 128>), dim3(num_tasks), dim3(kThreads), 0, st, a);
+      if (ahead)
+        hipLaunchKernelGGL((decode_kernel<__bf16, 128, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<__bf16, 128, false>), grid, block, 0, st, a);
       launch_combine<__bf16, 128>(combines_dev, num_combines, nullptr, a, st);
     } else {
-      hipLaunchKernelGGL((decode_kernel<__bf16, 64>), dim3(num_tasks), dim3(kThreads), 0, st, a);
+      if (ahead)
+        hipLaunchKernelGGL((decode_kernel<__bf16, 64, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<__bf16, 64, false>), grid, block, 0, st, a);
       launch_combine<__bf16, 64>(combines_dev, num_combines, nullptr, a, st);
     }
   } else {
     if (head_dim == 128) {
-      hipLaunchKernelGGL((decode_kernel<float, 128>), dim3(num_tasks), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<float, 128, false>), grid, block, 0, st, a);
       launch_combine<float, 128>(combines_dev, num_combines, nullptr, a, st);
     } else {
-      hipLaunchKernelGGL((decode_kernel<float, 64>), dim3(num_tasks), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<float, 64, false>), grid, block, 0, st, a);
       launch_combine<float, 64>(combines_dev, num_combines, nullptr, a, st);
     }
   }
