@@ -58,7 +58,7 @@ TILING = {
     "mixed_bf16": dict(dec_split=4096, pf_q_tile=128, pf_kv_split=0),
     # 4-row drafts: verify tasks (one task reads each KV page once for 4 rows x 4 heads), and
     # for comparison the same batch decomposed into prefill tiles (one per query head)
-    "verify_gqa_bf16": dict(dec_split=8192, verify_rows=4),
+    "verify_gqa_bf16": dict(dec_split=16384, verify_rows=4),
     "verify_gqa_bf16:as_prefill_tiles": dict(pf_q_tile=128, pf_kv_split=0, verify_rows=0),
     # the MHA decode batch over fp8 pages (half the KV bytes of the bf16 headline), and the
     # verify batch over fp8 pages
