@@ -66,3 +66,31 @@ def test_shared_decode_full_size_sampled():
     assert _has_shared(plan)
     import torch
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("shared_min", [0, 64])
+def test_decode_entry_and_unified_launch_agree_bitwise(shared_min):
+    """The decode entry (one chunk of page reads in flight per wave on tables with shared-prefix
+    tasks, two otherwise) and the unified launch (always two) run the same arithmetic in the same
+    order in every wave, so on one decode table, with or without shared-prefix groups, their
+    outputs agree bit for bit."""
+    import math
+    import torch
+    import paged_variable_length_amd as pa
+    rng = np.random.default_rng(77 + shared_min)
+    w = _decode_groups(rng, 4, 16, 16, 4, 128)
+    _announce(f"decode entry vs unified launch, shared_min={shared_min} N={w.num_seqs}")
+    vals = {k: v.to("cuda") for k, v in synth.make_values(w, device="cpu").items()}
+    plan = pa.StepPlan(w.q_lens, w.ctx_lens, w.block_table, w.num_q_heads, w.num_kv_heads,
+                       w.head_dim, w.block_size, device="cuda", dec_split=128,
+                       shared_min=shared_min)
+    assert _has_shared(plan) == bool(shared_min)
+    plan.write_cache(vals["k_new"], vals["v_new"], vals["k_pages"], vals["v_pages"])
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out_d = torch.full_like(vals["q"], float("nan"))
+    out_v = torch.full_like(vals["q"], float("nan"))
+    plan.decode(vals["q"], vals["k_pages"], vals["v_pages"], scale, out_d)
+    plan.varlen(vals["q"], vals["k_pages"], vals["v_pages"], scale, out_v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_d).all()
+    assert torch.equal(out_d.view(torch.int16), out_v.view(torch.int16))
