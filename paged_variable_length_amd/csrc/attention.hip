@@ -14,7 +14,11 @@
 // layout; V rows are loaded 16 bytes per lane along D and rearranged in registers, so the
 // value product O^T = V^T P^T consumes them without an LDS round trip and each lane ends up
 // owning one head's slice of D. Online softmax in base 2, per head; the four waves merge
-// through LDS at the end and write either the output row or an fp32 partial.
+// through LDS at the end and write either the output row or an fp32 partial. Block ids come
+// from scalar loads a chunk ahead; page reads carry the non-temporal hint where nothing in the
+// launch re-reads them (decode tables, and unified tables without prefill tiles), and a wave
+// keeps one chunk of reads in flight (three waves per SIMD, tables with shared-prefix tasks)
+// or two (two waves per SIMD, everything else).
 //
 // Prefill body (MFMA-bound). A task is (sequence, query head, up to 128 query rows, key
 // range). 64-key K and V tiles are gathered through the block table into two LDS buffers
