@@ -744,11 +744,12 @@ __device__ void decode_task_f32(const AttnArgs& a, const pa_task& t, float* smem
 // Lane-dependent LDS addresses are computed once per task; buffer, key block and k-step
 // enter as instruction offsets or as one XOR on a single base register.
 // ------------------------------------------------------------------------------------------
-template <int D>
+// CODES: the tiles hold fp8 codes (1 byte per element) instead of bf16 values.
+template <int D, bool CODES = false>
 struct PrefillCfg {
   static constexpr int kTile = 64;                                  // keys per LDS tile
-  static constexpr int kRowBytes = D * 2;                           // one bf16 key row
-  static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
+  static constexpr int kRowBytes = CODES ? D : D * 2;               // one key row
+  static constexpr int kChunks = kRowBytes / 16;                    // 16-byte chunks per row
   static constexpr int kTileBytes = kTile * kRowBytes;
   static constexpr int kKeysPerLoad = 1024 / kRowBytes;             // keys per wave load
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;       // per tensor per tile
@@ -763,9 +764,18 @@ struct PrefillCfg {
 // LDS time of both read patterns against a 3-bit pattern and matches an unswizzled
 // contiguous read. With 8 chunks per row (D = 64) a 3-bit pattern is used. The pattern
 // depends on key & 15 only, so shifting a key by a multiple of 16 keeps its pattern.
-template <int D>
+// Rows of fp8 codes (CODES, D = 128: 8 chunks of 16 codes): chunk c of key row r sits at
+// c ^ s(r), s(r) = 2*r1 + r2 + 4*r3 for key bits r1, r2, r3. With 64 banks of 4 bytes a row
+// covers half the banks, so rows of opposite parity share a bank line. Sixteen consecutive rows
+// reading one chunk (the K operand reads) take the eight chunk positions within each parity
+// (s is a permutation of 0..7 over bits 1-3); a transposed read takes rows {4g + 0..3,
+// 8 + 4g + 0..3} (g = 0, 1) at two neighbouring chunks, and s >> 1 differs between the four
+// rows of each parity there, so its sixteen half-chunk segments per parity meet no bank twice.
+template <int D, bool CODES = false>
 __device__ __forceinline__ int lds_swz(int key) {
-  if constexpr (D == 128)
+  if constexpr (CODES)
+    return 2 * ((key >> 1) & 1) + ((key >> 2) & 1) + 4 * ((key >> 3) & 1);
+  else if constexpr (D == 128)
     return ((key & 3) << 2) | ((key >> 2) & 3);
   else
     return ((key & 3) << 1) | ((key >> 2) & 1);
@@ -802,6 +812,11 @@ __device__ __forceinline__ int lds_swz(int key) {
   }
 PA_LDS_READ(ds_read_b128, u32x4)
 PA_LDS_READ(ds_read_b64_tr_b16, u32x2)
+// ds_read_b64_tr_b8 (probed on gfx950): within each 16-lane group, lane j = 8r + c returns
+// byte c of the 8-byte segments addressed by lanes r, r+2, ..., r+14. With lane k of the group
+// addressing key kbase + k/2, byte offset d0 + 8*(k%2) of a row of codes, lane j receives the
+// eight keys kbase .. kbase+7 at d = d0 + j.
+PA_LDS_READ(ds_read_b64_tr_b8, u32x2)
 #undef PA_LDS_READ
 
 template <int K, typename T>
@@ -843,14 +858,23 @@ __device__ __forceinline__ void mask_block(f32x16& s, int lim) {
   s[14] = mask_one<BASE + 26>(s[14], lim, ninf); s[15] = mask_one<BASE + 27>(s[15], lim, ninf);
 }
 
-// FP8: the pages hold E4M3FN codes with a power-of-two scale per page and tensor. A wave then
-// loads its share of a tile into registers (8 codes per lane and piece, the same elements the
-// direct load would move), and after the tile's compute converts them exactly to bf16 and
-// writes them where the direct load would have put them: the LDS layout, the buffers and the
-// compute are those of the bf16 pages.
-template <int D, bool FP8 = false>
+// MODE 0: bf16 pages. MODE 1 (FP8) and 2 (CODES): the pages hold E4M3FN codes with a
+// power-of-two scale per page and tensor.
+// FP8: a wave loads its share of a tile into registers (8 codes per lane and piece, the same
+// elements the direct load would move), and after the tile's compute converts them exactly to
+// bf16 and writes them where the direct load would have put them: the LDS layout, the buffers
+// and the compute are those of the bf16 pages.
+// CODES (D = 128): the direct loads move the codes themselves into LDS (half the bytes of a
+// bf16 tile) and every operand read converts them: a K read returns 16 codes of one key (the
+// operands of two k-steps, in a permuted d order that q follows), a transposed V read 8 keys
+// of one d; each is converted with the scale of its key's page. The loads, buffers and their
+// protocol are those of the bf16 pages.
+template <int D, int MODE = 0>
 __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
-  typedef PrefillCfg<D> C;
+  constexpr bool FP8 = MODE == 1;
+  constexpr bool CODES = MODE == 2;
+  static_assert(!CODES || D == 128, "codes in LDS are laid out for D = 128");
+  typedef PrefillCfg<D, CODES> C;
   constexpr int KS = D / 16;   // k-steps of the QK product
   constexpr int NB = D / 32;   // 32-row d blocks of O^T
   constexpr int P = C::kLoadsPerWave;
@@ -879,17 +903,21 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
 
   bf16x8 qf[KS];
   {
+    // CODES: k-step 2j takes d = 32j + 16*g2 + 0..7 and k-step 2j+1 d = 32j + 16*g2 + 8..15,
+    // the order in which a K read returns a key's codes
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(cu0 + qi) * a.num_q_heads + h) * D + 8 * g2;
+                         (static_cast<size_t>(cu0 + qi) * a.num_q_heads + h) * D +
+                         (CODES ? 16 : 8) * g2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      if (row_ok)
+        v = *reinterpret_cast<const u32x4*>(qp + (CODES ? 32 * (ks >> 1) + 8 * (ks & 1) : 16 * ks));
       qf[ks] = as_bf16x8(v);
     }
   }
 
-  constexpr int EB = FP8 ? 1 : 2;           // bytes per element in the pages
+  constexpr int EB = FP8 || CODES ? 1 : 2;  // bytes per element in the pages
   const size_t head_stride = static_cast<size_t>(bs) * D;
   const size_t block_stride = static_cast<size_t>(a.num_kv_heads) * head_stride;
   const char* kbase = static_cast<const char*>(a.k_pages) + kvh * head_stride * EB;
@@ -902,7 +930,7 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
   // K row i32, chunk 2*ks + g2. The row base is a multiple of 256 bytes and k-step ks only
   // flips chunk bits 1..3, so the address of k-step ks is ka0 ^ (ks << 5).
-  uint32_t ka0 = lds0 + i32 * C::kRowBytes + ((g2 ^ lds_swz<D>(i32)) << 4);
+  uint32_t ka0 = lds0 + i32 * C::kRowBytes + ((g2 ^ lds_swz<D, CODES>(i32)) << 4);
   const int gq = lane >> 4, jq = lane & 15;
   const int v_key = 4 * g2 + (jq >> 2);     // key of this lane's segment (+ 16*kk, + 8)
   const int v_d = 16 * (gq & 1) + 4 * (jq & 3);
@@ -915,6 +943,19 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
       va[2 * n + hf] = lds0 + 2 * C::kTileBytes + key * C::kRowBytes +
                        ((((32 * n + v_d) >> 3) ^ lds_swz<D>(key)) << 4) + 8 * (jq & 1);
     }
+  // CODES: transposed V reads of codes. Byte b of lane i32 + 32*g2's result must be the key of
+  // its k-slot b in the P operand, 4*g2 + b%4 + 8*(b/4) (+ 16*kk: the keys the score layout gives
+  // that lane), at d = 32n + i32. Lane j of a 16-lane group receives its byte b from the
+  // segment of lane 2b + j/8, so lane (gq, jq) addresses key 4*(gq/2) + (jq/2)%4 + 8*(jq/8) at
+  // d = 32n + 16*(gq%2) + 8*(jq%2): the V^T operand of d block n and k-step kk.
+  uint32_t vca[NB] = {};
+  if constexpr (CODES) {
+    const int key = 4 * (gq >> 1) + ((jq >> 1) & 3) + 8 * (jq >> 3);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      vca[n] = lds0 + 2 * C::kTileBytes + key * C::kRowBytes +
+               (((2 * n + (gq & 1)) ^ lds_swz<D, true>(key)) << 4) + 8 * (jq & 1);
+  }
   // ---- direct-load addressing. Each wave loads 16 consecutive keys of every tile
   // (P pieces of kKeysPerLoad keys). Tiles start at multiples of 64 keys and blocks hold at
   // least 16 keys, so those 16 keys lie in one block: one wave-uniform block id per tile (a
@@ -925,9 +966,10 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   // (dma0 ^ (swizzle difference << 4)) + 1024*i, the last term an instruction offset.
   const int key0 = wave_u * P * C::kKeysPerLoad + lane / C::kChunks;
   uint32_t dma0 = (key0 & (bs - 1)) * C::kRowBytes +
-                        (((lane % C::kChunks) ^ lds_swz<D>(key0)) << 4);
+                        (((lane % C::kChunks) ^ lds_swz<D, CODES>(key0)) << 4);
   auto dma_off = [&](int i) -> uint32_t {
-    return dma0 ^ ((lds_swz<D>(key0 + i * C::kKeysPerLoad) ^ lds_swz<D>(key0)) << 4);
+    return dma0 ^
+           ((lds_swz<D, CODES>(key0 + i * C::kKeysPerLoad) ^ lds_swz<D, CODES>(key0)) << 4);
   };
   // The pieces' lane offsets within a tile, dma_off(i) + 1024*i (fp8: half of it, the offset of
   // the same elements' codes), computed once and held across the loop (P registers): each load
@@ -943,6 +985,17 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
   auto block_id = [&](int tile) -> int {
     const int kp = min(kv0 + tile * C::kTile + wave_u * P * C::kKeysPerLoad, kv1 - 1);
     return bt[kp >> a.bs_shift];
+  };
+  // CODES: page scales of the four 16-key groups of tile `tile` (each group one wave's direct
+  // loads, so one page), K (which 0) or V (1); clamped like the loads
+  float ksc4[4], vsc4[4];
+  auto tile_scales = [&](int tile, int which, float (&out)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kp = min(kv0 + tile * C::kTile + 16 * g, kv1 - 1);
+      const size_t page = static_cast<size_t>(bt[kp >> a.bs_shift]) * a.num_kv_heads + kvh;
+      out[g] = ((cfloat*)a.scales)[2 * page + which];
+    }
   };
   // fp8 staging: codes of the K (0) and V (1) pieces in flight, and their pages' scales
   u32x2 stage[2][P];
@@ -1088,17 +1141,53 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     }
     // four matrix steps on key block KB_, k-steps KS0..KS0+3 from kw, each followed by one
     // word of exponentials (words W0..W0+3)
-    auto group = [&](f32x16& acc_s, const u32x4 (&kw)[4], int ks0, int w0) {
+    // (`step(q)`, CODES: the conversion of one operand of the next group, beside matrix step q)
+    auto group = [&](f32x16& acc_s, const u32x4 (&kw)[4], int ks0, int w0, auto step) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (QK)
           acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw[q]), qf[ks0 + q], acc_s, 0, 0, 0);
         if constexpr (EXP) exp_word(w0 + q);
+        step(q);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    auto none = [](int) {};
     u32x4 k0[4], k1[4];
-    if constexpr (KS == 8) {
+    if constexpr (CODES) {
+      // read j of key block kb: the 16 codes of k-steps 2j and 2j+1 of key i32 + 32kb, taken
+      // times the scale of the key's page (keys 0-15 and 16-31 of a block lie in two groups)
+      const float sk0 = i32 < 16 ? ksc4[0] : ksc4[1];
+      const float sk1 = i32 < 16 ? ksc4[2] : ksc4[3];
+      const uint32_t kc[4] = {ka0, ka0 ^ (1u << 5), ka0 ^ (2u << 5), ka0 ^ (3u << 5)};
+      // operand q of a group: the low (q even) or high (q odd) 8 codes of read q/2 of the pair
+      auto conv1 = [&](const u32x4& cw, bool hi, float sc) -> u32x4 {
+        const uint32_t w0 = hi ? cw[2] : cw[0], w1 = hi ? cw[3] : cw[1];
+        return u32x4{fp8x2_to_bf16x2<false>(w0, sc), fp8x2_to_bf16x2<true>(w0, sc),
+                     fp8x2_to_bf16x2<false>(w1, sc), fp8x2_to_bf16x2<true>(w1, sc)};
+      };
+      // two operand sets used in turn: the next group's operands are converted one per matrix
+      // step of the current group
+      u32x4 kwa[4], kwb[4];
+      if constexpr (QK) {
+        ds_read_b128_x4_issue<KOFF>(kc, k0);
+        ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kc, k1);
+        lds_wait<4>(k0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kwa[q] = conv1(k0[q >> 1], q & 1, sk0);
+      }
+      group(sn[0], kwa, 0, 0, [&](int q) {
+        if constexpr (QK) kwb[q] = conv1(k0[2 + (q >> 1)], q & 1, sk0);
+      });
+      if constexpr (QK) lds_wait<0>(k1);
+      group(sn[0], kwb, 4, 4, [&](int q) {
+        if constexpr (QK) kwa[q] = conv1(k1[q >> 1], q & 1, sk1);
+      });
+      group(sn[1], kwa, 0, 8, [&](int q) {
+        if constexpr (QK) kwb[q] = conv1(k1[2 + (q >> 1)], q & 1, sk1);
+      });
+      group(sn[1], kwb, 4, 12, none);
+    } else if constexpr (KS == 8) {
       const uint32_t kl[4] = {ka0, ka0 ^ (1u << 5), ka0 ^ (2u << 5), ka0 ^ (3u << 5)};
       const uint32_t kh[4] = {ka0 ^ (4u << 5), ka0 ^ (5u << 5), ka0 ^ (6u << 5), ka0 ^ (7u << 5)};
       if constexpr (QK) {
@@ -1106,19 +1195,19 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         ds_read_b128_x4_issue<KOFF>(kh, k1);
         lds_wait<4>(k0);
       }
-      group(sn[0], k0, 0, 0);
+      group(sn[0], k0, 0, 0, none);
       if constexpr (QK) {
         ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kl, k0);
         lds_wait<4>(k1);
       }
-      group(sn[0], k1, 4, 4);
+      group(sn[0], k1, 4, 4, none);
       if constexpr (QK) {
         ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kh, k1);
         lds_wait<4>(k0);
       }
-      group(sn[1], k0, 0, 8);
+      group(sn[1], k0, 0, 8, none);
       if constexpr (QK) lds_wait<0>(k1);
-      group(sn[1], k1, 4, 12);
+      group(sn[1], k1, 4, 12, none);
     } else {
       const uint32_t kl[4] = {ka0, ka0 ^ (1u << 5), ka0 ^ (2u << 5), ka0 ^ (3u << 5)};
       if constexpr (QK) {
@@ -1126,9 +1215,9 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
         ds_read_b128_x4_issue<KOFF + 32 * C::kRowBytes>(kl, k1);
         lds_wait<4>(k0);
       }
-      group(sn[0], k0, 0, 0);
+      group(sn[0], k0, 0, 0, none);
       if constexpr (QK) lds_wait<0>(k1);
-      group(sn[1], k1, 0, 4);
+      group(sn[1], k1, 0, 4, none);
       if constexpr (EXP) {
 #pragma unroll
         for (int w = 8; w < 16; ++w) exp_word(w);
@@ -1176,11 +1265,14 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
                      auto hook) {
     constexpr int VOFF = decltype(vb_tag)::value * C::kTileBytes;
     constexpr bool PV = decltype(do_pv)::value, MAX = decltype(do_max)::value;
-    typedef u32x2 VR[NR];
+    constexpr int NV = CODES ? NB : NR;     // reads per k-step batch
+    typedef u32x2 VR[NV];
     VR vr0, vr1;
     auto v_issue = [&](auto kk_tag, VR& r) {
       constexpr int KK = decltype(kk_tag)::value;
-      if constexpr (NR == 8)
+      if constexpr (CODES)
+        ds_read_b64_tr_b8_x4_issue<VOFF + 16 * KK * C::kRowBytes>(vca, r);
+      else if constexpr (NR == 8)
         ds_read_b64_tr_b16_x8_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
       else
         ds_read_b64_tr_b16_x4_issue<VOFF + 16 * KK * C::kRowBytes>(va, r);
@@ -1197,11 +1289,26 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     constexpr int kMaxPer = 32 / (4 * NB);  // scores folded per matrix step
     auto pv = [&](int kk, VR& r) {
       const bf16x8 pf = as_bf16x8(pw[kk]);
+      // CODES: keys 16kk + 0..15 lie in group kk, one page scale for the k-step; the operand of
+      // matrix step n+1 is converted beside step n
+      const float sv = CODES ? vsc4[kk] : 0.f;
+      auto vconv = [&](int n) -> u32x4 {
+        return u32x4{fp8x2_to_bf16x2<false>(r[n][0], sv), fp8x2_to_bf16x2<true>(r[n][0], sv),
+                     fp8x2_to_bf16x2<false>(r[n][1], sv), fp8x2_to_bf16x2<true>(r[n][1], sv)};
+      };
+      u32x4 vnext;
+      if constexpr (CODES && PV) vnext = vconv(0);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         if constexpr (PV) {
-          const u32x4 vw = {r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
+          u32x4 vw;
+          if constexpr (CODES)
+            vw = vnext;
+          else
+            vw = u32x4{r[2 * n][0], r[2 * n][1], r[2 * n + 1][0], r[2 * n + 1][1]};
           acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, acc[n], 0, 0, 0);
+          if constexpr (CODES)
+            if (n + 1 < NB) vnext = vconv(n + 1);
         }
         if constexpr (MAX) {
 #pragma unroll
@@ -1216,19 +1323,19 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     if constexpr (PV) {
       v_issue(std::integral_constant<int, 0>(), vr0);
       v_issue(std::integral_constant<int, 1>(), vr1);
-      lds_wait<NR>(vr0);
+      lds_wait<NV>(vr0);
     }
     pv(0, vr0);
     hook(0);
     if constexpr (PV) {
       v_issue(std::integral_constant<int, 2>(), vr0);
-      lds_wait<NR>(vr1);
+      lds_wait<NV>(vr1);
     }
     pv(1, vr1);
     hook(1);
     if constexpr (PV) {
       v_issue(std::integral_constant<int, 3>(), vr1);
-      lds_wait<NR>(vr0);
+      lds_wait<NV>(vr0);
     }
     pv(2, vr0);
     hook(2);
@@ -1270,6 +1377,7 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  if constexpr (CODES) tile_scales(0, 0, ksc4);
   if (nw > 0) {
     float unused;
     phase_a(I0(), T_(), F_(), sa, sb, unused);
@@ -1308,6 +1416,12 @@ __device__ void prefill_task(const AttnArgs& a, const pa_task& t, char* smem) {
     // offset operand next to the scalar base
 #pragma unroll
     for (int i = 0; i < P; ++i) asm volatile("" : "+v"(dmo[i]));
+    if constexpr (CODES) {
+      // page scales of the tiles this iteration reads: K(j+1), V(j) (scalar loads, ahead of
+      // the barrier's wait)
+      tile_scales(j + 1, 0, ksc4);
+      tile_scales(j, 1, vsc4);
+    }
     if (j > 0 || ntiles > 2) {
       if constexpr (FP8) {
         lds_barrier();
@@ -1451,12 +1565,14 @@ __global__ __launch_bounds__(kThreads, 2) void meta_attn_kernel(AttnArgs a) {
 // The unified launch over fp8 pages: every task kind, rows addressed through cu_seqlens.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void meta_attn_fp8_kernel(AttnArgs a) {
-  constexpr size_t kPrefill = PrefillCfg<D>::kSmemBytes;
+  // D = 128: codes in LDS, converted at the operand reads; D = 64: converted on the way in
+  constexpr int kMode = D == 128 ? 2 : 1;
+  constexpr size_t kPrefill = PrefillCfg<D, kMode == 2>::kSmemBytes;
   constexpr size_t kDecode = kMergeFloats<D> * sizeof(float);
   __shared__ __attribute__((aligned(1024))) char smem[kPrefill > kDecode ? kPrefill : kDecode];
   const pa_task t = a.tasks[xcd_remap(blockIdx.x, a.num_tasks)];
   if (t.kind == PA_TASK_PREFILL)
-    prefill_task<D, true>(a, t, smem);
+    prefill_task<D, kMode>(a, t, smem);
   else if (a.stream_reads)
     decode_task_fp8<D, true>(a, t, reinterpret_cast<float*>(smem));
   else
