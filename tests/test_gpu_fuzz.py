@@ -24,7 +24,7 @@ def _batch(rng, max_seqs, decode_only):
     return q, ctx
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_mixed_batches(seed):
     """Unified launch (bf16) over a random mix of decode rows, short drafts and prefill chunks."""
     rng = np.random.default_rng(7000 + seed)
@@ -42,7 +42,7 @@ def test_random_mixed_batches(seed):
     small_case(w, "varlen", **tiling)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_random_decode_batches(seed, dtype):
     """Decode entry over random single-row batches (bf16 and fp32 pages)."""
@@ -57,7 +57,7 @@ def test_random_decode_batches(seed, dtype):
     small_case(w, "decode", dec_split=int(rng.choice([64, 256, 1024])))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_mixed_batches_fp8(seed):
     """Unified launch over fp8 pages, on the same random space as the bf16 batches."""
     from tests.test_gpu_fp8_varlen import fp8_case
