@@ -74,3 +74,30 @@ def test_random_mixed_batches_fp8(seed):
     w = synth.custom_workload(q, ctx, hkv * g, hkv, d, bs, seed=seed,
                               spare_blocks=int(rng.integers(0, 4)))
     fp8_case(w, values_on="cpu", **tiling)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shared_prefix_batches(seed):
+    """Shared-prefix groups on random shapes: decode groups through the decode entry (even
+    seeds), or aliased groups between prefill and verify rows through the unified launch (odd
+    seeds); group sizes, prefix lengths, G, block size, split size and grouping threshold drawn
+    jointly."""
+    from tests.helpers import aliased_workload
+    rng = np.random.default_rng(9500 + seed)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    shared_min = int(rng.choice([64, 128, 256]))
+    dec_split = int(rng.choice([64, 128, 256, 1024]))   # shared tables: multiples of 64 keys
+    if seed % 2 == 0:
+        n_groups = int(rng.integers(1, 5))
+        prefix = rng.integers(1, 40, size=n_groups) * bs
+        own = [rng.integers(1, 300, size=int(rng.integers(1, 20))) for _ in range(n_groups)]
+        w = synth.shared_prefix_workload(prefix, own, hkv * g, hkv, d, bs, seed=seed,
+                                         spare_blocks=int(rng.integers(0, 4)))
+        small_case(w, "decode", dec_split=dec_split, shared_min=shared_min)
+    else:
+        w = aliased_workload(rng, bs, int(rng.integers(2, 7)), hkv * g, hkv, d, seed=seed)
+        small_case(w, "varlen", dec_split=dec_split, pf_q_tile=int(rng.choice([32, 64, 128])),
+                   verify_rows=int(rng.choice([0, 4])), shared_min=shared_min)
