@@ -175,3 +175,26 @@ def test_gemm_empty_and_errors():
         pa.smooth_gemm(a, torch.zeros(3, 8, dtype=torch.bfloat16, device=DEV),
                        torch.zeros(4, 3, dtype=torch.bfloat16, device=DEV), 64,
                        plan.tasks, plan.reduces, 0, None)
+
+
+def _random_gemm_case(seed):
+    """Shape, tile, split, balancing and base offsets of random case `seed` (host draws only)."""
+    rng = np.random.default_rng(12000 + seed)
+    M, N = int(rng.integers(1, 1100)), int(rng.integers(1, 900))
+    K = int(rng.choice([int(rng.integers(1, 2100)), 8 * int(rng.integers(1, 260))]))
+    tile = int(rng.choice([128, 256]))
+    k_split = int(rng.choice([0, 0, 64, 192, 512]))
+    tail = bool(k_split == 0 and rng.integers(0, 2))
+    workers = int(rng.choice([3, 40, 256]))
+    off = int(rng.choice([0, 0, 0, 1]))
+    return M, N, K, tile, k_split, tail, workers, off
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_gemm_random(seed):
+    """Random shapes (ragged M and N, K aligned or not), tiles, K splits, tail splits and
+    operand bases drawn jointly; every element against the oracle, nothing stored past C."""
+    M, N, K, tile, k_split, tail, workers, off = _random_gemm_case(seed)
+    c, a, w, _ = _run(M, N, K, tile, k_split, seed=seed, a_offset=off, w_offset=2 * off,
+                      workers=workers, tail=tail)
+    _check(c, a, w, what=f"random {seed}: {M}x{N}x{K}")
