@@ -101,3 +101,58 @@ def test_random_shared_prefix_batches(seed):
         w = aliased_workload(rng, bs, int(rng.integers(2, 7)), hkv * g, hkv, d, seed=seed)
         small_case(w, "varlen", dec_split=dec_split, pf_q_tile=int(rng.choice([32, 64, 128])),
                    verify_rows=int(rng.choice([0, 4])), shared_min=shared_min)
+
+
+def _cache_batch(seed):
+    """Random lengths and shapes of a cache-write case (host draws only)."""
+    rng = np.random.default_rng(11000 + seed)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    q, ctx = _batch(rng, 12, decode_only=False)
+    return rng, q, ctx, hkv, d, bs
+
+
+@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_random_cache_writes(seed, dtype):
+    """reshape_and_cache on random batches (decode appends, drafts, chunks over prefixes, any
+    block size and head shape): the pages bit for bit against the oracle's scatter, every other
+    slot untouched."""
+    import torch
+    import paged_variable_length_amd as pa
+    from oracle import cache as oc
+    from tests.helpers import to_np_raw
+    rng, q, ctx, hkv, d, bs = _cache_batch(seed)
+    w = synth.custom_workload(q, ctx, hkv, hkv, d, bs, dtype=dtype, seed=seed,
+                              spare_blocks=int(rng.integers(0, 4)))
+    print(f"\n[case] cache write {dtype} seed={seed} N={w.num_seqs} T={w.num_tokens} "
+          f"Hkv={hkv} D={d} bs={bs}", flush=True)
+    vals = {k: v.to("cuda") for k, v in synth.make_values(w, device="cpu").items()}
+    before_k, before_v = to_np_raw(vals["k_pages"]).copy(), to_np_raw(vals["v_pages"]).copy()
+    plan = pa.StepPlan(w.q_lens, w.ctx_lens, w.block_table, hkv, hkv, d, bs, device="cuda")
+    plan.write_cache(vals["k_new"], vals["v_new"], vals["k_pages"], vals["v_pages"])
+    torch.cuda.synchronize()
+    ek, ev = oc.reshape_and_cache(to_np_raw(vals["k_new"]), to_np_raw(vals["v_new"]), before_k,
+                                  before_v, w.block_table, w.q_lens, w.ctx_lens)
+    assert np.array_equal(to_np_raw(vals["k_pages"]).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(to_np_raw(vals["v_pages"]).view(np.uint8), ev.view(np.uint8))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_cache_writes_fp8(seed):
+    """The fp8 cache write on random batches: codes and page scales bit for bit against the
+    fp8 oracle (pages rescaled when a new row raises their maximum), other pages untouched."""
+    from tests.test_gpu_fp8 import _assert_pages_equal, _gpu_write, _oracle_write
+    import paged_variable_length_amd as pa
+    rng, q, ctx, hkv, d, bs = _cache_batch(seed)
+    w = synth.custom_workload(q, ctx, 2 * hkv, hkv, d, bs, seed=seed,
+                              spare_blocks=int(rng.integers(0, 4)))
+    print(f"\n[case] fp8 cache write seed={seed} N={w.num_seqs} T={w.num_tokens} "
+          f"Hkv={hkv} D={d} bs={bs}", flush=True)
+    vals = {k: v.to("cuda") for k, v in synth.make_values(w, device="cpu").items()}
+    pages = {k: v.to("cuda") for k, v in synth.make_fp8_pages(w).items()}
+    ref = _oracle_write(w, vals, pages)
+    plan = pa.StepPlan(w.q_lens, w.ctx_lens, w.block_table, 2 * hkv, hkv, d, bs, device="cuda")
+    _gpu_write(w, vals, pages, plan)
+    _assert_pages_equal(pages, ref)
