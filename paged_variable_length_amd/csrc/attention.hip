@@ -1,11 +1,16 @@
 // HIP kernels and launchers of libpagedattn.so, written for gfx950 (MI355X, CDNA4).
 //
 // Kernels
-//   reshape_and_cache_kernel  copy of new K/V rows into their page slots (HBM-bound copy)
-//   decode_kernel             split-K decode attention, one workgroup per decode task
-//   meta_attn_kernel          one grid over a mixed, load-sorted task table: each workgroup
-//                             reads its task's kind and runs the decode or the prefill body
-//   combine_kernel            log-sum-exp merge of split partials into `out`
+//   reshape_and_cache_kernel      copy of new K/V rows into their page slots (HBM-bound copy)
+//   reshape_and_cache_fp8_kernel  the same into fp8 pages: each touched page is re-encoded
+//                                 with a power-of-two scale covering its old and new rows
+//   decode_kernel                 split-K decode attention, one workgroup per decode task
+//   decode_fp8_kernel             the same over fp8 pages (codes converted in registers)
+//   meta_attn_kernel              one grid over a mixed, load-sorted task table: each
+//                                 workgroup reads its task's kind and runs the decode or the
+//                                 prefill body
+//   meta_attn_fp8_kernel          the same over fp8 pages
+//   combine_kernel                log-sum-exp merge of split partials into `out`
 //
 // Decode body (HBM-bound). A task is (sequence, kv head, key range). Its four waves take
 // interleaved chunks of the key range. Scores S = K Q^T come from 16x16x32 bf16 MFMAs whose
@@ -25,7 +30,10 @@
 // each; each wave owns 32 query rows, computes S^T = K Q^T and O^T += V^T P^T with 32x32x16
 // bf16 MFMAs, and applies the causal mask only on tiles that cross the diagonal. The tile
 // loop is software-pipelined: the scores of tile j+1 are formed while the exponentials of
-// tile j are, and the value product of tile j runs beside the maximum of tile j+1.
+// tile j are, and the value product of tile j runs beside the maximum of tile j+1. Each
+// iteration's direct loads are issued together right after its barrier. Over fp8 pages the
+// tiles hold the codes themselves at D = 128 (converted with the page scales at the operand
+// reads) and converted bf16 values at D = 64 (converted on their way into LDS).
 #include <hip/hip_runtime.h>
 
 #include <climits>
